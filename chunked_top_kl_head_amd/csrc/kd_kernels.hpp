@@ -1,0 +1,546 @@
+// kd_kernels.hpp -- epilogues of the three contractions and the per-row
+// kernels of the fused chunked top-K KL loss.
+//
+// Pages cited: [TH] ai-thai.com/posts/846 (Thai translation of "Efficient
+// Knowledge Distillation for LLMs: Offline Top-K Logits and a Fused Chunked KL
+// Loss"), section "Fused Chunked KL Loss", items "Dense KL" and "Fused chunked
+// KL"; [TA] scitechpulse.com/ta (Tamil report on the same post), closing
+// paragraph (the backward recomputes each slice, doubling projection work).
+//
+// Notation: a = z / tau are the student logits of one chunk row over the full
+// vocabulary; everything inside a chunk is carried in base 2, y = a * log2(e),
+// so that the hardware exp2/log2 apply directly.  lse values handed across
+// the boundary are natural-log.
+#pragma once
+
+#include "kd_gemm.hpp"
+
+namespace kd {
+
+enum LogitsMode { kStats = 0, kFused = 1, kBwd = 2 };
+
+// Per-call scalars kept at the head of the workspace.
+struct WsHeader {
+    double loss_acc;   // running sum of row losses (fixed chunk order)
+    int64_t N;         // number of kept positions
+    float s;           // g / (tau N), 0 when N = 0
+    float pad[11];
+};
+static_assert(sizeof(WsHeader) <= 256, "header slot");
+
+// ---------------------------------------------------------------------------
+// Logit-tile epilogue: the tile is Z^T (rows = vocabulary ids v, columns =
+// chunk rows t).  Per column it reduces the tile's 256 ids to a partial
+// (max, sum of exp) in base 2 -- the online logsumexp of [TH] "Fused chunked
+// KL" is this tiled max/sum plus a merge in the row kernel.
+//   kStats: write the partials only (forward).
+//   kFused: also write e = exp2(y - tile max) as the MFMA operand of the
+//           gradient GEMMs (rescaled to G in place by the row kernel).
+//   kBwd  : lse is known: write the dense part of G, s * exp(a - lse), directly.
+// ---------------------------------------------------------------------------
+struct LogitsParams {
+    f32x2* stats;          // [C][nvt] (max2, sum) per (row, vocab tile)
+    void* E;               // [C][V_pad] element type of the operands
+    int V, V_pad, nvt, rows;
+    float scale2;          // log2(e) / tau
+    const float* lse;      // kBwd: natural-log lse of the chunk rows
+    const uint8_t* ignore; // kBwd: ignore flags of the chunk rows (may be null)
+    const WsHeader* hdr;   // kBwd: s
+};
+
+template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
+    using Params = LogitsParams;
+    static constexpr int FM = BM / 32, FN = BN / 32;
+
+    static __device__ __forceinline__ void store4(const Params& p, int t, int v0, float x0, float x1,
+                                                  float x2, float x3) {
+        if constexpr (Elem<E>::size == 2) {
+            u32x2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.E) + (int64_t)t * p.V_pad + v0) = w;
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.E) + (int64_t)t * p.V_pad + v0) =
+                f32x4{x0, x1, x2, x3};
+        }
+    }
+
+    static __device__ __forceinline__ void apply(WaveMma<E, BM, BN>& mma, int m0, int n0, int /*split*/,
+                                                 int wm, int wn, int lane, int tid, char* smem,
+                                                 const Params& p) {
+        const int lr = lane & 15, lc = lane >> 4;
+        // base-2 logits; ids at or beyond V are excluded (-inf)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = (m0 + wm * (BM / 2) + 16 * i + 4 * lc + r) < p.V;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    mma.acc[i][j][r] = ok ? mma.acc[i][j][r] * p.scale2 : -INFINITY;
+            }
+
+        if constexpr (MODE == kBwd) {
+            const float s = p.hdr->s;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int t = n0 + wn * (BN / 2) + 16 * j + lr;
+                if (t >= p.rows) continue;
+                const bool kept = (p.ignore == nullptr) || (p.ignore[t] == 0);
+                const float st = kept ? s : 0.f;
+                const float l2 = p.lse[t] * kLog2e;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    float g[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) g[r] = st * fast_exp2(mma.acc[i][j][r] - l2);
+                    store4(p, t, m0 + wm * (BM / 2) + 16 * i + 4 * lc, g[0], g[1], g[2], g[3]);
+                }
+            }
+            return;
+        } else {
+            float* red = reinterpret_cast<float*>(smem);   // [4][BN]: max of wm=0,1 then sum of wm=0,1
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, mma.acc[i][j][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                if (lc == 0) red[wm * BN + wn * (BN / 2) + 16 * j + lr] = mx;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = wn * (BN / 2) + 16 * j + lr;
+                const float M = fmaxf(red[n], red[BN + n]);
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = fast_exp2(mma.acc[i][j][r] - M);
+                        mma.acc[i][j][r] = e;
+                        s += e;
+                    }
+                s += __shfl_xor(s, 16, kWave);
+                s += __shfl_xor(s, 32, kWave);
+                if (lc == 0) red[(2 + wm) * BN + n] = s;
+            }
+            __syncthreads();
+            if (tid < BN) {
+                const int t = n0 + tid;
+                if (t < p.rows) {
+                    const f32x2 st = {fmaxf(red[tid], red[BN + tid]), red[2 * BN + tid] + red[3 * BN + tid]};
+                    p.stats[(int64_t)t * p.nvt + m0 / BM] = st;
+                }
+            }
+            if constexpr (MODE == kFused) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int t = n0 + wn * (BN / 2) + 16 * j + lr;
+                    if (t >= p.rows) continue;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+                        store4(p, t, m0 + wm * (BM / 2) + 16 * i + 4 * lc, mma.acc[i][j][0],
+                               mma.acc[i][j][1], mma.acc[i][j][2], mma.acc[i][j][3]);
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// grad_H epilogue: tile of dH^T (rows = hidden index j, columns = chunk rows t).
+// One split writes grad_H directly; several splits write fp32 partials that a
+// fixed-order reduction sums.
+// ---------------------------------------------------------------------------
+struct GradHParams {
+    void* out;        // grad_H of the chunk's first row (element type)
+    float* partial;   // [splits][C][d] fp32
+    int d, rows, C, direct;
+};
+
+template <typename E, int BM, int BN> struct GradHEpi {
+    using Params = GradHParams;
+    static constexpr int FM = BM / 32, FN = BN / 32;
+    static __device__ __forceinline__ void apply(WaveMma<E, BM, BN>& mma, int m0, int n0, int split,
+                                                 int wm, int wn, int lane, int, char*, const Params& p) {
+        const int lr = lane & 15, lc = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int t = n0 + wn * (BN / 2) + 16 * j + lr;
+            if (t >= p.rows) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int h = m0 + wm * (BM / 2) + 16 * i + 4 * lc;
+                if (h >= p.d) continue;
+                const f32x4 v = mma.acc[i][j];
+                if (p.direct) {
+                    if constexpr (Elem<E>::size == 2) {
+                        u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)t * p.d + h) = w;
+                    } else {
+                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)t * p.d + h) = v;
+                    }
+                } else {
+                    *reinterpret_cast<f32x4*>(p.partial + ((int64_t)split * p.C + t) * p.d + h) = v;
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// grad_W epilogue: tile of dW^T (rows = hidden index j, columns = vocab ids v),
+// written to (first chunk) or added to (later chunks) the fp32 grad_W[V][d].
+// Every element has one owner per chunk: no atomics, fixed chunk order.
+// ---------------------------------------------------------------------------
+struct GradWParams {
+    float* gw;
+    int d, V, accumulate;
+};
+
+template <typename E, int BM, int BN> struct GradWEpi {
+    using Params = GradWParams;
+    static constexpr int FM = BM / 32, FN = BN / 32;
+    static __device__ __forceinline__ void apply(WaveMma<E, BM, BN>& mma, int m0, int n0, int,
+                                                 int wm, int wn, int lane, int, char*, const Params& p) {
+        const int lr = lane & 15, lc = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int v = n0 + wn * (BN / 2) + 16 * j + lr;
+            if (v >= p.V) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int h = m0 + wm * (BM / 2) + 16 * i + 4 * lc;
+                if (h >= p.d) continue;
+                f32x4* dst = reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h);
+                f32x4 val = mma.acc[i][j];
+                if (p.accumulate) val += *dst;
+                *dst = val;
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Block reductions (256 threads)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_max(float v, float* sh) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Prepass: N, s = g / (tau N), loss accumulator reset.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void prepass_kernel(WsHeader* hdr, const uint8_t* ignore, int64_t T,
+                                                           const float* grad_loss, float tau) {
+    __shared__ float sh[4];
+    int64_t cnt = 0;
+    for (int64_t t = threadIdx.x; t < T; t += kThreads) cnt += (ignore == nullptr || ignore[t] == 0);
+    // counts are exact in fp32 up to 2^24 per thread; sum per wave in integers
+    int64_t c = cnt;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, kWave);
+    __shared__ int64_t shc[4];
+    if ((threadIdx.x & 63) == 0) shc[threadIdx.x >> 6] = c;
+    __syncthreads();
+    (void)sh;
+    if (threadIdx.x == 0) {
+        const int64_t N = shc[0] + shc[1] + shc[2] + shc[3];
+        const float g = grad_loss ? *grad_loss : 1.0f;
+        hdr->N = N;
+        hdr->s = N > 0 ? g / (tau * (float)N) : 0.f;
+        hdr->loss_acc = 0.0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row kernel: one workgroup per chunk row.
+//   merge the logit tiles' partials into lse (kStats / kFused),
+//   teacher softmax over the K cached logits ([TH] "Dense KL": the teacher
+//   distribution comes from the cached top-K logits),
+//   student logits at the cached ids as K dot products H_t . W_id,
+//   row loss  L = sum_k p_k (log p_k - a_k + lse),
+//   kFused: rescale the row's exp2(y - tile max) into G = s (q - P) in place,
+//   kFused/kBwd: replace the K cached entries by s (q - P).
+// ---------------------------------------------------------------------------
+struct RowParams {
+    int mode;
+    int t0, rows;
+    int d, V, V_pad, K, nvt;
+    float inv_tau;
+    const void* H;          // [T][d]
+    const void* W;          // [V][d]
+    const int32_t* idx;     // [T][K]
+    const float* logit;     // [T][K]
+    const uint8_t* ignore;  // [T] or null
+    const f32x2* stats;     // [C][nvt]
+    const float* lse_in;    // [T] (kBwd)
+    float* lse_out;         // [T] or null
+    float* row_loss;        // [T] or null
+    float* chunk_loss;      // [C]
+    void* G;                // [C][V_pad]
+    const WsHeader* hdr;
+};
+
+constexpr int kMaxK = 1024;
+
+template <typename E>
+__device__ __forceinline__ float dot_row(const E* h, const E* w, int d, int lane) {
+    float acc = 0.f;
+    if constexpr (Elem<E>::size == 2) {
+        const u32x4* hv = reinterpret_cast<const u32x4*>(h);
+        const u32x4* wv = reinterpret_cast<const u32x4*>(w);
+        for (int c = lane; c < d / 8; c += kWave) {
+            const u32x4 a = hv[c], b = wv[c];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = fmaf(bf16_bits_to_f32(a[q] & 0xFFFFu), bf16_bits_to_f32(b[q] & 0xFFFFu), acc);
+                acc = fmaf(bf16_bits_to_f32(a[q] >> 16), bf16_bits_to_f32(b[q] >> 16), acc);
+            }
+        }
+    } else {
+        const f32x4* hv = reinterpret_cast<const f32x4*>(h);
+        const f32x4* wv = reinterpret_cast<const f32x4*>(w);
+        for (int c = lane; c < d / 4; c += kWave) {
+            const f32x4 a = hv[c], b = wv[c];
+            acc = fmaf(a[0], b[0], acc);
+            acc = fmaf(a[1], b[1], acc);
+            acc = fmaf(a[2], b[2], acc);
+            acc = fmaf(a[3], b[3], acc);
+        }
+    }
+    return wave_sum(acc);
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
+    extern __shared__ float dyn[];           // nvt floats (kFused rescale factors)
+    __shared__ float sh_p[kMaxK], sh_lp[kMaxK], sh_a[kMaxK];
+    __shared__ int sh_id[kMaxK];
+    __shared__ float red[4];
+    const int r = (int)blockIdx.x;
+    const int t = p.t0 + r;
+    const int tid = (int)threadIdx.x;
+    const bool kept = (p.ignore == nullptr) || (p.ignore[t] == 0);
+
+    // 1. lse of the row
+    float lse2;
+    if (p.mode != kBwd) {
+        const f32x2* st = p.stats + (int64_t)r * p.nvt;
+        float M = -INFINITY, S = 0.f;
+        for (int i = tid; i < p.nvt; i += kThreads) {
+            const f32x2 v = st[i];
+            const float Mn = fmaxf(M, v[0]);
+            if (Mn > -INFINITY) S = S * fast_exp2(M - Mn) + v[1] * fast_exp2(v[0] - Mn);
+            M = Mn;
+        }
+        const float Mall = block_max(M, red);
+        const float Sall = block_sum(M > -INFINITY ? S * fast_exp2(M - Mall) : 0.f, red);
+        lse2 = Mall + fast_log2(Sall);
+        if (tid == 0 && p.lse_out) p.lse_out[t] = lse2 * kLn2;
+    } else {
+        lse2 = p.lse_in[t] * kLog2e;
+    }
+
+    const int64_t grow = (int64_t)r * p.V_pad;
+    if (!kept) {
+        if (p.mode != kBwd) {
+            if (tid == 0) {
+                p.chunk_loss[r] = 0.f;
+                if (p.row_loss) p.row_loss[t] = 0.f;
+            }
+        }
+        if (p.mode == kFused) {
+            u32x4* g = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.G) + grow * Elem<E>::size);
+            const int nch = p.V_pad * Elem<E>::size / 16;
+            for (int c = tid; c < nch; c += kThreads) g[c] = u32x4{0u, 0u, 0u, 0u};
+        }
+        return;
+    }
+
+    // 2. teacher distribution over the cached entries
+    const int K = p.K;
+    float bmax = -INFINITY;
+    for (int k = tid; k < K; k += kThreads) {
+        const float b = p.logit[(int64_t)t * K + k] * p.inv_tau;
+        sh_lp[k] = b;
+        sh_id[k] = clamp_id(p.idx[(int64_t)t * K + k], p.V);
+        bmax = fmaxf(bmax, b);
+    }
+    bmax = block_max(bmax, red);
+    float esum = 0.f;
+    for (int k = tid; k < K; k += kThreads) esum += fast_exp2((sh_lp[k] - bmax) * kLog2e);
+    esum = block_sum(esum, red);
+    const float logS = fast_log2(esum) * kLn2;
+    for (int k = tid; k < K; k += kThreads) {
+        const float lp = sh_lp[k] - bmax - logS;
+        sh_lp[k] = lp;
+        sh_p[k] = fast_exp2(lp * kLog2e);
+    }
+
+    // 3. student logits at the cached ids
+    const int wave = tid >> 6, lane = tid & 63;
+    const E* hrow = reinterpret_cast<const E*>(p.H) + (int64_t)t * p.d;
+    for (int k = wave; k < K; k += kThreads / kWave) {
+        const E* wrow = reinterpret_cast<const E*>(p.W) + (int64_t)sh_id[k] * p.d;
+        const float z = dot_row<E>(hrow, wrow, p.d, lane);
+        if (lane == 0) sh_a[k] = z * p.inv_tau;
+    }
+    __syncthreads();
+    const float lse = lse2 * kLn2;
+
+    // 4. row loss (entries with p = 0 contribute 0)
+    if (p.mode != kBwd) {
+        float L = 0.f;
+        for (int k = tid; k < K; k += kThreads)
+            if (sh_p[k] > 0.f) L += sh_p[k] * (sh_lp[k] - sh_a[k] + lse);
+        L = block_sum(L, red);
+        if (tid == 0) {
+            p.chunk_loss[r] = L;
+            if (p.row_loss) p.row_loss[t] = L;
+        }
+        if (p.mode == kStats) return;
+    }
+
+    const float s = p.hdr->s;
+    // 5. kFused: e * 2^(tile max - lse2) * s  ->  dense part of G
+    if (p.mode == kFused) {
+        const f32x2* st = p.stats + (int64_t)r * p.nvt;
+        for (int i = tid; i < p.nvt; i += kThreads) dyn[i] = s * fast_exp2(st[i][0] - lse2);
+        __syncthreads();
+        if constexpr (Elem<E>::size == 2) {
+            u32x4* g = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.G) + grow);
+            const int nch = p.V_pad / 8;
+            for (int c = tid; c < nch; c += kThreads) {
+                const float f = dyn[(c * 8) / 256];
+                u32x4 v = g[c];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    v[q] = pack_bf16x2(bf16_bits_to_f32(v[q] & 0xFFFFu) * f, bf16_bits_to_f32(v[q] >> 16) * f);
+                g[c] = v;
+            }
+        } else {
+            f32x4* g = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.G) + grow);
+            const int nch = p.V_pad / 4;
+            for (int c = tid; c < nch; c += kThreads) {
+                const float f = dyn[(c * 4) / 256];
+                g[c] = g[c] * f;
+            }
+        }
+        __syncthreads();
+    }
+
+    // 6. cached entries: G = s (q - P), P summing duplicate ids; first occurrence writes
+    for (int k = tid; k < K; k += kThreads) {
+        const int id = sh_id[k];
+        bool first = true;
+        for (int k2 = 0; k2 < k; ++k2) first &= (sh_id[k2] != id);
+        if (!first) continue;
+        float P = sh_p[k];
+        for (int k2 = k + 1; k2 < K; ++k2) P += (sh_id[k2] == id) ? sh_p[k2] : 0.f;
+        const float q = fast_exp2(sh_a[k] * kLog2e - lse2);
+        const float gval = s * (q - P);
+        if constexpr (Elem<E>::size == 2) {
+            reinterpret_cast<uint16_t*>(p.G)[grow + id] = (uint16_t)(pack_bf16x2(gval, 0.f) & 0xFFFFu);
+        } else {
+            reinterpret_cast<float*>(p.G)[grow + id] = gval;
+        }
+    }
+}
+
+// Sum of the chunk's row losses in a fixed order, added to the running total.
+__global__ __launch_bounds__(kThreads) void loss_chunk_kernel(WsHeader* hdr, const float* chunk_loss, int rows) {
+    __shared__ double sh[kThreads];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < rows; i += kThreads) acc += (double)chunk_loss[i];
+    sh[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) hdr->loss_acc += sh[0];
+}
+
+__global__ void loss_final_kernel(const WsHeader* hdr, float* loss) {
+    if (threadIdx.x == 0 && blockIdx.x == 0)
+        *loss = hdr->N > 0 ? (float)(hdr->loss_acc / (double)hdr->N) : 0.f;
+}
+
+// grad_H rows of a chunk = fixed-order sum of the split partials.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void gradh_reduce_kernel(void* out, const float* partial, int rows,
+                                                                int d, int C, int splits) {
+    const int64_t n4 = (int64_t)rows * d / 4;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t e = i * 4;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(partial + e);
+        for (int s = 1; s < splits; ++s)
+            acc += *reinterpret_cast<const f32x4*>(partial + (int64_t)s * C * d + e);
+        if constexpr (Elem<E>::size == 2) {
+            u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + e) = w;
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e) = acc;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_kernel(u32x4* p, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kThreads)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Precondition check: ids outside [0, V) and kept rows without a finite teacher logit.
+__global__ __launch_bounds__(kThreads) void validate_kernel(const int32_t* idx, const float* logit,
+                                                            const uint8_t* ignore, int64_t T, int K, int V,
+                                                            unsigned long long* bad) {
+    const int64_t t = blockIdx.x;
+    if (t >= T) return;
+    if (ignore && ignore[t]) return;
+    unsigned long long nbad = 0;
+    int finite = 0, nan = 0;
+    for (int k = threadIdx.x; k < K; k += kThreads) {
+        const int id = idx[t * K + k];
+        nbad += (id < 0 || id >= V);
+        const float l = logit[t * K + k];
+        nan |= (l != l);
+        finite |= (l > -INFINITY && l == l);
+    }
+    __shared__ int shf[kThreads], shn[kThreads];
+    __shared__ unsigned long long shb[kThreads];
+    shf[threadIdx.x] = finite;
+    shn[threadIdx.x] = nan;
+    shb[threadIdx.x] = nbad;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int f = 0, n = 0;
+        unsigned long long b = 0;
+        for (int i = 0; i < kThreads; ++i) { f |= shf[i]; n |= shn[i]; b += shb[i]; }
+        b += (!f || n) ? 1ull : 0ull;
+        if (b) atomicAdd(bad, b);
+    }
+}
+
+__global__ void set_zero_u64(unsigned long long* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0ull;
+}
+
+}  // namespace kd

@@ -1,0 +1,369 @@
+// kd_topk_kl.hip -- C ABI and host-side chunk scheduler of the fused chunked
+// top-K KL distillation loss on MI355X (gfx950).
+//
+// Pages cited: [TH] ai-thai.com/posts/846 (Thai translation of "Efficient
+// Knowledge Distillation for LLMs: Offline Top-K Logits and a Fused Chunked KL
+// Loss"), section "Fused Chunked KL Loss", item "Fused chunked KL": the
+// sequence is processed slice by slice, each slice's logits are formed from
+// the hidden states, folded into the loss and dropped, the backward pass
+// recomputes them, and memory grows linearly with the sequence length.
+//
+// Per chunk of C rows the scheduler enqueues, on the caller's stream:
+//   forward : logits GEMM (tile max/sum partials) -> row kernel (lse, teacher,
+//             gather, row loss) -> chunk loss sum
+//   backward: logits GEMM recomputed with the forward's lse (dense G) -> row
+//             kernel (cached-id entries of G) -> grad_H GEMM -> grad_W GEMM
+//   fused   : logits GEMM (partials + softmax numerators) -> row kernel (lse,
+//             loss, G in place) -> grad_H GEMM -> grad_W GEMM
+// The workspace holds one chunk's G (C x V_pad) and partials, so its size is
+// independent of T; the T-sized arrays are the caller's inputs and outputs.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kd_kernels.hpp"
+#include "kd_topk_kl.h"
+
+namespace kd {
+
+constexpr int BM = 256, BN = 256;      // output tile of every contraction
+constexpr int64_t kOperandLimit = (int64_t)1 << 31;
+
+template <typename E, bool AK, bool BK, class Epi>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(Operand A, Operand B, GemmGeom g, typename Epi::Params ep) {
+    __shared__ __attribute__((aligned(16))) char smem[gemm_lds_bytes<BM, BN>()];
+    gemm_body<E, BM, BN, AK, BK, Epi>(A, B, g, ep, smem);
+}
+
+struct Plan {
+    int64_t T, d, V, K, C;
+    int es;               // element size of H, W, G
+    int64_t V_pad, nvt;
+    float tau;
+    int splits;           // grad_H splits over the vocabulary
+    size_t off_hdr, off_closs, off_stats, off_G, off_part, total;
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static int64_t default_chunk(int64_t d, int64_t V, int es) {
+    (void)d;
+    const int64_t V_pad = cdiv(V, BM) * BM;
+    int64_t C = 4096;
+    while (C > 256 && C * V_pad * es >= kOperandLimit) C -= 256;
+    return C;
+}
+
+static int choose_splits(int64_t tiles, int64_t K, int bk) {
+    if (tiles >= 512) return 1;
+    int best = 1;
+    double best_eff = 0.0;
+    for (int s = 1; s <= 16; ++s) {
+        if (s > 1 && K / s < 8 * bk) break;
+        const int64_t wg = tiles * s;
+        const double eff = (double)wg / (double)(cdiv(wg, 256) * 256);
+        if (eff >= 0.92) return s;
+        if (eff > best_eff + 1e-12) { best_eff = eff; best = s; }
+    }
+    return best;
+}
+
+static kd_status check_problem(const kd_problem* p) {
+    if (!p) return KD_ERR_NULL;
+    if (p->T < 0 || p->d < 1 || p->V < 1 || p->K < 1 || p->K > p->V || p->chunk < 0) return KD_ERR_SHAPE;
+    if (!std::isfinite(p->temperature) || !(p->temperature > 0.f)) return KD_ERR_VALUE;
+    if (p->dtype != KD_BF16 && p->dtype != KD_F32) return KD_ERR_UNSUPPORTED;
+    if (p->d % 8 != 0 || p->K > kMaxK || p->V > ((int64_t)1 << 21)) return KD_ERR_UNSUPPORTED;
+    return KD_OK;
+}
+
+static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
+    kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (op != KD_OP_FORWARD && op != KD_OP_BACKWARD && op != KD_OP_FUSED) return KD_ERR_VALUE;
+    Plan q{};
+    q.T = p->T; q.d = p->d; q.V = p->V; q.K = p->K;
+    q.es = p->dtype == KD_BF16 ? 2 : 4;
+    q.tau = p->temperature;
+    q.V_pad = cdiv(q.V, BM) * BM;
+    q.nvt = q.V_pad / BM;
+    q.C = p->chunk > 0 ? p->chunk : default_chunk(q.d, q.V, q.es);
+    // operand extents addressed with 32-bit buffer offsets
+    if (q.V * q.d * q.es >= kOperandLimit || q.C * q.V_pad * q.es >= kOperandLimit ||
+        q.C * q.d * q.es >= kOperandLimit || q.C > (1 << 24))
+        return KD_ERR_UNSUPPORTED;
+    const int bk = 128 / q.es;
+    q.splits = choose_splits(cdiv(q.d, BM) * cdiv(q.C, BN), q.V_pad, bk);
+    size_t o = 0;
+    q.off_hdr = o;   o += 256;
+    q.off_closs = o; o = align256(o + sizeof(float) * (size_t)q.C);
+    q.off_stats = o;
+    if (op != KD_OP_BACKWARD) o = align256(o + sizeof(f32x2) * (size_t)(q.C * q.nvt));
+    q.off_G = o;
+    if (op != KD_OP_FORWARD) o = align256(o + (size_t)(q.C * q.V_pad * q.es));
+    q.off_part = o;
+    if (op != KD_OP_FORWARD && q.splits > 1) o = align256(o + sizeof(float) * (size_t)(q.splits * q.C * q.d));
+    q.total = o;
+    *pl = q;
+    return KD_OK;
+}
+
+static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static GemmGeom geom(int64_t M, int64_t N, int64_t K, int splits, int bk, int n_fastest) {
+    GemmGeom g;
+    g.M = (int)M; g.N = (int)N; g.K = (int)K;
+    g.tiles_m = (int)cdiv(M, BM);
+    g.tiles_n = (int)cdiv(N, BN);
+    g.k_per_split = (int)(cdiv(cdiv(K, splits), bk) * bk);
+    g.n_fastest = n_fastest;
+    return g;
+}
+
+static dim3 gemm_grid(const GemmGeom& g, int splits) {
+    const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n;
+    return dim3((unsigned)(cdiv(tiles, 8) * 8), (unsigned)splits, 1);
+}
+
+static inline Operand operand(const void* ptr, int64_t ld, int64_t bytes) {
+    Operand o;
+    o.ptr = ptr; o.ld = ld; o.bytes = (uint32_t)bytes;
+    return o;
+}
+
+// One op over all chunks.  All pointers already validated.
+template <typename E>
+static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, const int32_t* idx,
+                     const float* logit, const uint8_t* ignore, const float* grad_loss, float* loss,
+                     const float* lse_in, float* lse_out, float* row_loss, void* grad_H, float* grad_W,
+                     void* ws, hipStream_t stream) {
+    char* wsb = static_cast<char*>(ws);
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(wsb + pl.off_hdr);
+    float* closs = reinterpret_cast<float*>(wsb + pl.off_closs);
+    f32x2* stats = reinterpret_cast<f32x2*>(wsb + pl.off_stats);
+    void* G = wsb + pl.off_G;
+    float* part = reinterpret_cast<float*>(wsb + pl.off_part);
+    const int es = pl.es, bk = 128 / es;
+    const bool want_grads = op != KD_OP_FORWARD;
+    const bool want_loss = op != KD_OP_BACKWARD;
+
+    hipLaunchKernelGGL(prepass_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, ignore, pl.T, grad_loss, pl.tau);
+    if (want_grads && pl.T == 0) {
+        const int64_t n16 = pl.V * pl.d * 4 / 16;
+        hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(kThreads), 0, stream, reinterpret_cast<u32x4*>(grad_W), n16);
+    }
+    const float scale2 = kLog2e / pl.tau;
+    for (int64_t t0 = 0; t0 < pl.T; t0 += pl.C) {
+        const int64_t rc = pl.T - t0 < pl.C ? pl.T - t0 : pl.C;
+        const char* Hc = static_cast<const char*>(H) + t0 * pl.d * es;
+        // ---- logits GEMM: Z^T = W H_c^T (M = V_pad, N = rc, K = d)
+        {
+            const Operand A = operand(W, pl.d, pl.V * pl.d * es);
+            const Operand B = operand(Hc, pl.d, rc * pl.d * es);
+            const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk, 1);
+            LogitsParams lp{};
+            lp.stats = stats; lp.E = G; lp.V = (int)pl.V; lp.V_pad = (int)pl.V_pad; lp.nvt = (int)pl.nvt;
+            lp.rows = (int)rc; lp.scale2 = scale2; lp.hdr = hdr;
+            lp.lse = lse_in ? lse_in + t0 : nullptr;
+            lp.ignore = ignore ? ignore + t0 : nullptr;
+            const dim3 grid = gemm_grid(g, 1);
+            if (op == KD_OP_FORWARD)
+                hipLaunchKernelGGL((gemm_kernel<E, true, true, LogitsEpi<E, BM, BN, kStats>>), grid, dim3(kThreads), 0, stream, A, B, g, lp);
+            else if (op == KD_OP_FUSED)
+                hipLaunchKernelGGL((gemm_kernel<E, true, true, LogitsEpi<E, BM, BN, kFused>>), grid, dim3(kThreads), 0, stream, A, B, g, lp);
+            else
+                hipLaunchKernelGGL((gemm_kernel<E, true, true, LogitsEpi<E, BM, BN, kBwd>>), grid, dim3(kThreads), 0, stream, A, B, g, lp);
+        }
+        // ---- row kernel
+        {
+            RowParams rp{};
+            rp.mode = op == KD_OP_FORWARD ? kStats : (op == KD_OP_FUSED ? kFused : kBwd);
+            rp.t0 = (int)t0; rp.rows = (int)rc;
+            rp.d = (int)pl.d; rp.V = (int)pl.V; rp.V_pad = (int)pl.V_pad; rp.K = (int)pl.K; rp.nvt = (int)pl.nvt;
+            rp.inv_tau = 1.0f / pl.tau;
+            rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.ignore = ignore;
+            rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss;
+            rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
+            hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), (size_t)(pl.nvt * sizeof(float)),
+                               stream, rp);
+        }
+        if (want_loss)
+            hipLaunchKernelGGL(loss_chunk_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, closs, (int)rc);
+        if (!want_grads) continue;
+        // ---- grad_H^T = W^T G^T (M = d, N = rc, K = V_pad)
+        {
+            const Operand A = operand(W, pl.d, pl.V * pl.d * es);
+            const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
+            const GemmGeom g = geom(pl.d, rc, pl.V_pad, pl.splits, bk, 1);
+            GradHParams hp{};
+            hp.out = static_cast<char*>(grad_H) + t0 * pl.d * es;
+            hp.partial = part; hp.d = (int)pl.d; hp.rows = (int)rc; hp.C = (int)pl.C;
+            hp.direct = pl.splits == 1;
+            hipLaunchKernelGGL((gemm_kernel<E, false, true, GradHEpi<E, BM, BN>>), gemm_grid(g, pl.splits),
+                               dim3(kThreads), 0, stream, A, B, g, hp);
+            if (pl.splits > 1) {
+                const int64_t n4 = rc * pl.d / 4;
+                const unsigned blocks = (unsigned)(cdiv(n4, kThreads) < 2048 ? cdiv(n4, kThreads) : 2048);
+                hipLaunchKernelGGL(gradh_reduce_kernel<E>, dim3(blocks), dim3(kThreads), 0, stream, hp.out, part,
+                                   (int)rc, (int)pl.d, (int)pl.C, pl.splits);
+            }
+        }
+        // ---- grad_W^T (+)= H_c^T G (M = d, N = V_pad, K = rc)
+        {
+            const Operand A = operand(Hc, pl.d, rc * pl.d * es);
+            const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
+            const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 0);
+            GradWParams wp{};
+            wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0;
+            hipLaunchKernelGGL((gemm_kernel<E, false, false, GradWEpi<E, BM, BN>>), gemm_grid(g, 1), dim3(kThreads), 0,
+                               stream, A, B, g, wp);
+        }
+    }
+    if (want_loss) hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, stream, hdr, loss);
+    return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
+}
+
+static kd_status dispatch(const Plan& pl, int dtype, kd_op op, const void* H, const void* W, const int32_t* idx,
+                          const float* logit, const uint8_t* ignore, const float* grad_loss, float* loss,
+                          const float* lse_in, float* lse_out, float* row_loss, void* grad_H, float* grad_W,
+                          void* ws, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // clear a stale error so the status reflects this call's launches
+    if (dtype == KD_BF16)
+        return run<bf16_t>(pl, op, H, W, idx, logit, ignore, grad_loss, loss, lse_in, lse_out, row_loss, grad_H,
+                           grad_W, ws, s);
+    return run<float>(pl, op, H, W, idx, logit, ignore, grad_loss, loss, lse_in, lse_out, row_loss, grad_H, grad_W,
+                      ws, s);
+}
+
+}  // namespace kd
+
+using namespace kd;
+
+// Common argument checks: inputs present and aligned, workspace large enough.
+static kd_status check_common(const kd_problem* p, kd_op op, const void* H, const void* W, const int32_t* idx,
+                              const float* logit, void* ws, size_t ws_bytes, Plan* pl) {
+    kd_status st = make_plan(p, op, pl);
+    if (st != KD_OK) return st;
+    if (!W) return KD_ERR_NULL;
+    if (p->T > 0 && (!H || !idx || !logit)) return KD_ERR_NULL;
+    if (pl->total > 0 && !ws) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(ws, 16) || !aligned(idx, 4) || !aligned(logit, 4))
+        return KD_ERR_ALIGN;
+    if (ws_bytes < pl->total) return KD_ERR_WORKSPACE;
+    return KD_OK;
+}
+
+extern "C" {
+
+int64_t kd_topk_kl_default_chunk(const kd_problem* prob) {
+    if (check_problem(prob) != KD_OK) return 0;
+    return default_chunk(prob->d, prob->V, prob->dtype == KD_BF16 ? 2 : 4);
+}
+
+kd_status kd_topk_kl_workspace_size(const kd_problem* prob, kd_op op, size_t* bytes) {
+    try {
+        if (!bytes) return KD_ERR_NULL;
+        Plan pl;
+        kd_status st = make_plan(prob, op, &pl);
+        if (st != KD_OK) return st;
+        *bytes = pl.total;
+        return KD_OK;
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_topk_kl_forward(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
+                             const float* topk_logit, const uint8_t* ignore, float* loss, float* lse, float* row_loss,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        Plan pl;
+        kd_status st = check_common(prob, KD_OP_FORWARD, H, W, topk_idx, topk_logit, workspace, workspace_bytes, &pl);
+        if (st != KD_OK) return st;
+        if (!loss || (prob->T > 0 && !lse)) return KD_ERR_NULL;
+        if (!aligned(loss, 4) || !aligned(lse, 4) || !aligned(row_loss, 4)) return KD_ERR_ALIGN;
+        return dispatch(pl, prob->dtype, KD_OP_FORWARD, H, W, topk_idx, topk_logit, ignore, nullptr, loss, nullptr,
+                        lse, row_loss, nullptr, nullptr, workspace, stream);
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_topk_kl_backward(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
+                              const float* topk_logit, const uint8_t* ignore, const float* lse,
+                              const float* grad_loss, void* grad_H, float* grad_W, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    try {
+        Plan pl;
+        kd_status st = check_common(prob, KD_OP_BACKWARD, H, W, topk_idx, topk_logit, workspace, workspace_bytes, &pl);
+        if (st != KD_OK) return st;
+        if (!grad_W || (prob->T > 0 && (!lse || !grad_H))) return KD_ERR_NULL;
+        if (!aligned(grad_H, 16) || !aligned(grad_W, 16) || !aligned(lse, 4) || !aligned(grad_loss, 4))
+            return KD_ERR_ALIGN;
+        return dispatch(pl, prob->dtype, KD_OP_BACKWARD, H, W, topk_idx, topk_logit, ignore, grad_loss, nullptr, lse,
+                        nullptr, nullptr, grad_H, grad_W, workspace, stream);
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
+                           const float* topk_logit, const uint8_t* ignore, const float* grad_loss, float* loss,
+                           float* lse, float* row_loss, void* grad_H, float* grad_W, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    try {
+        Plan pl;
+        kd_status st = check_common(prob, KD_OP_FUSED, H, W, topk_idx, topk_logit, workspace, workspace_bytes, &pl);
+        if (st != KD_OK) return st;
+        if (!loss || !grad_W || (prob->T > 0 && !grad_H)) return KD_ERR_NULL;
+        if (!aligned(loss, 4) || !aligned(lse, 4) || !aligned(row_loss, 4) || !aligned(grad_loss, 4) ||
+            !aligned(grad_H, 16) || !aligned(grad_W, 16))
+            return KD_ERR_ALIGN;
+        return dispatch(pl, prob->dtype, KD_OP_FUSED, H, W, topk_idx, topk_logit, ignore, grad_loss, loss, nullptr,
+                        lse, row_loss, grad_H, grad_W, workspace, stream);
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx, const float* topk_logit,
+                              const uint8_t* ignore, int64_t* bad_count, void* stream) {
+    try {
+        kd_status st = check_problem(prob);
+        if (st != KD_OK) return st;
+        if (!bad_count || (prob->T > 0 && (!topk_idx || !topk_logit))) return KD_ERR_NULL;
+        if (!aligned(bad_count, 8) || !aligned(topk_idx, 4) || !aligned(topk_logit, 4)) return KD_ERR_ALIGN;
+        if (prob->T > 0x7FFFFFFF) return KD_ERR_UNSUPPORTED;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        (void)hipGetLastError();
+        unsigned long long* bc = reinterpret_cast<unsigned long long*>(bad_count);
+        hipLaunchKernelGGL(set_zero_u64, dim3(1), dim3(64), 0, s, bc);
+        if (prob->T > 0)
+            hipLaunchKernelGGL(validate_kernel, dim3((unsigned)prob->T), dim3(kThreads), 0, s, topk_idx, topk_logit,
+                               ignore, prob->T, (int)prob->K, (int)prob->V, bc);
+        return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+const char* kd_status_string(kd_status status) {
+    switch (status) {
+        case KD_OK: return "ok";
+        case KD_ERR_NULL: return "a required pointer is NULL";
+        case KD_ERR_SHAPE: return "invalid shape (T, d, V, K or chunk)";
+        case KD_ERR_VALUE: return "invalid value (temperature must be finite and > 0)";
+        case KD_ERR_ALIGN: return "misaligned pointer";
+        case KD_ERR_WORKSPACE: return "workspace smaller than kd_topk_kl_workspace_size";
+        case KD_ERR_UNSUPPORTED: return "unsupported problem (dtype, d % 8, K > 1024 or size limits)";
+        case KD_ERR_HIP: return "HIP launch failure";
+        case KD_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

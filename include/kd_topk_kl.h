@@ -1,0 +1,152 @@
+/*
+ * kd_topk_kl.h -- C ABI of the MI355X (gfx950) fused chunked top-K KL
+ * distillation loss.
+ *
+ * The operation.  A student's final projection (lm_head) is fused into a
+ * KL-divergence distillation loss against an offline teacher cache that keeps,
+ * per position, only the teacher's top-K token ids and logits.  Positions are
+ * processed in chunks of C rows: each chunk's logits H_c W^T are formed,
+ * consumed and discarded, so the T x V student logit matrix never exists, and
+ * the backward pass recomputes a chunk's logits instead of storing them.
+ * Sources (web pages describing the method; they give no formulas or code):
+ *   [TH] ai-thai.com/posts/846, Thai translation of the Hugging Face post
+ *        "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a
+ *        Fused Chunked KL Loss": section "Offline distillation" (the top-100
+ *        cache), section "Fused Chunked KL Loss", items "Dense KL" (teacher
+ *        distribution rebuilt from the cached logits), "Fused chunked KL"
+ *        (projection fused into the loss, per-slice logits discarded, backward
+ *        recomputes each slice, memory linear in sequence length).
+ *   [RU] iitog.ru, "Multiverse Computing сократила видеопамять для дистилляции
+ *        нейросетей до 15,6 раза": the paragraph on the two system changes.
+ * Definition (the plain reading of those passages; the pages fix no formula):
+ *   a_tv   = (H_t . W_v) / tau                     student logits over the full vocabulary
+ *   lse_t  = log sum_v exp(a_tv)                    (full-vocabulary logsumexp)
+ *   p_tk   = softmax_k(topk_logit_tk / tau)         teacher, renormalised over the K cached ids
+ *   L_t    = sum_k p_tk (log p_tk - a_{t,idx_tk} + lse_t)      = KL(p_t || q_t) on the cached ids
+ *   loss   = (1/N) sum_{t: ignore_t == 0} L_t,  N = #{t: ignore_t == 0}; loss = 0 when N = 0
+ *   G_tv   = g/(tau N) (exp(a_tv - lse_t) - P_tv),  P_tv = sum_{k: idx_tk = v} p_tk  (0 on ignored rows)
+ *   grad_H = G W,  grad_W = G^T H                   (g = upstream gradient of loss)
+ * There is no temperature-squared factor and no gradient to the teacher inputs.
+ *
+ * Memory and ownership.
+ *   - Every array argument is DEVICE memory owned by the caller; the library
+ *     allocates nothing and keeps no state between calls.  Scratch memory
+ *     comes from the caller's workspace, sized by kd_topk_kl_workspace_size;
+ *     its size depends on (C, V, K, d) and not on T.
+ *   - All work is enqueued on the caller's HIP stream (`stream`, a
+ *     hipStream_t; NULL = the default stream).  Calls return after enqueueing
+ *     and never synchronise; results are ready when the stream reaches them.
+ *   - Calls on different streams with separate workspaces may run
+ *     concurrently; two in-flight calls must not share a workspace.
+ *   - Results are run-to-run bitwise deterministic for a given problem,
+ *     chunk size and device (fixed reduction orders, no float atomics).
+ *
+ * Layouts (row-major, contiguous):
+ *   H          [T, d]  element type `dtype`
+ *   W          [V, d]  element type `dtype` (the nn.Linear weight layout)
+ *   topk_idx   [T, K]  int32, ids in [0, V)
+ *   topk_logit [T, K]  fp32 teacher logits (-inf allowed: probability 0)
+ *   ignore     [T]     uint8, non-zero = position excluded; NULL = none excluded
+ *   loss       [1]     fp32; lse, row_loss [T] fp32
+ *   grad_H     [T, d]  element type `dtype` (rounded to nearest even from fp32), overwritten
+ *   grad_W     [V, d]  fp32, overwritten
+ * Alignment: H, W, grad_H, grad_W and workspace 16 bytes; the fp32/int32
+ * arrays 4 bytes.  Outputs must not alias inputs or each other.
+ *
+ * Errors.  Every argument check runs on the host before anything is enqueued;
+ * on error nothing is enqueued and the outputs are untouched.  No C++
+ * exception crosses this interface.  Out-of-range ids and kept positions whose
+ * teacher logits are all -inf (or NaN) are preconditions, not checked on the
+ * hot path: they give undefined values but never an out-of-bounds memory
+ * access (ids are clamped into [0, V) before any load or store);
+ * kd_topk_kl_validate reports them.  Cache contents of ignored positions are
+ * never read.
+ */
+#ifndef KD_TOPK_KL_H
+#define KD_TOPK_KL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KD_OK = 0,
+    KD_ERR_NULL = 1,         /* a required pointer is NULL */
+    KD_ERR_SHAPE = 2,        /* T < 0, d < 1, V < 1, K < 1, K > V, chunk < 0 */
+    KD_ERR_VALUE = 3,        /* temperature not finite or <= 0 */
+    KD_ERR_ALIGN = 4,        /* a pointer violates the alignment above */
+    KD_ERR_WORKSPACE = 5,    /* workspace_bytes below kd_topk_kl_workspace_size */
+    KD_ERR_UNSUPPORTED = 6,  /* dtype unknown, d % 8 != 0, K > 1024, or sizes beyond the 2^31-byte operand limit */
+    KD_ERR_HIP = 7,          /* a HIP launch failed (asynchronous faults surface at the caller's next sync) */
+    KD_ERR_INTERNAL = 8
+} kd_status;
+
+typedef enum { KD_BF16 = 0, KD_F32 = 1 } kd_dtype;
+
+typedef enum { KD_OP_FORWARD = 0, KD_OP_BACKWARD = 1, KD_OP_FUSED = 2 } kd_op;
+
+typedef struct {
+    int64_t T;            /* positions (batch x sequence, flattened) */
+    int64_t d;            /* hidden size, multiple of 8 */
+    int64_t V;            /* vocabulary size */
+    int64_t K;            /* cached teacher entries per position, 1 <= K <= min(V, 1024) */
+    int64_t chunk;        /* rows per chunk C; 0 = library default (kd_topk_kl_default_chunk) */
+    int32_t dtype;        /* kd_dtype of H, W and grad_H */
+    float temperature;    /* tau > 0, divides both teacher and student logits */
+} kd_problem;
+
+/* Chunk size used when prob->chunk == 0 (depends on d, V and dtype only). */
+int64_t kd_topk_kl_default_chunk(const kd_problem* prob);
+
+/* Bytes of workspace `op` needs for `prob`; writes them to *bytes.  The value
+ * depends on (C, V, K, d, dtype), not on T. */
+kd_status kd_topk_kl_workspace_size(const kd_problem* prob, kd_op op, size_t* bytes);
+
+/* Forward ([TH] "Fused chunked KL": per chunk, project, take the
+ * full-vocabulary logsumexp, gather the student at the cached ids, accumulate,
+ * discard).  Writes loss[1], lse[T] (needed by kd_topk_kl_backward; written
+ * for every position, ignored ones too) and, if non-NULL, row_loss[T] (0 on
+ * ignored positions). */
+kd_status kd_topk_kl_forward(const kd_problem* prob, const void* H, const void* W,
+                             const int32_t* topk_idx, const float* topk_logit,
+                             const uint8_t* ignore, float* loss, float* lse, float* row_loss,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward ([TH] "Fused chunked KL": each chunk's logits are recomputed, not
+ * stored).  Takes lse[T] from kd_topk_kl_forward and the upstream gradient
+ * grad_loss[1] (device fp32; NULL means 1).  Overwrites grad_H[T, d] and
+ * grad_W[V, d]. */
+kd_status kd_topk_kl_backward(const kd_problem* prob, const void* H, const void* W,
+                              const int32_t* topk_idx, const float* topk_logit,
+                              const uint8_t* ignore, const float* lse, const float* grad_loss,
+                              void* grad_H, float* grad_W,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward and backward in one pass over the chunks (each chunk's logits are
+ * projected once and reused for the loss and the gradients).  Same outputs as
+ * the two calls above; lse and row_loss may be NULL. */
+kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W,
+                           const int32_t* topk_idx, const float* topk_logit,
+                           const uint8_t* ignore, const float* grad_loss,
+                           float* loss, float* lse, float* row_loss,
+                           void* grad_H, float* grad_W,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug check of the cache preconditions: writes to bad_count[0] (device
+ * int64) the number of ids outside [0, V) plus the number of kept positions
+ * whose teacher logits are all -inf or contain NaN. */
+kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx,
+                              const float* topk_logit, const uint8_t* ignore,
+                              int64_t* bad_count, void* stream);
+
+/* Static description of a status code. */
+const char* kd_status_string(kd_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_TOPK_KL_H */

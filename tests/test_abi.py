@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before enqueueing."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_top_kl_head_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kd_topk_kl.h")
+
+# fake but well-aligned device addresses: validation never dereferences them
+P16 = ctypes.c_void_p(0x100000)
+P16b = ctypes.c_void_p(0x200000)
+P4 = ctypes.c_void_p(0x300004)
+MIS = ctypes.c_void_p(0x400002)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from chunked_top_kl_head_amd import build
+        build.build()
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:kd_status|size_t|int64_t|const char\*)\s+(kd_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def prob(T=64, d=64, V=1000, K=10, chunk=0, dtype=B.KD_BF16, tau=1.0):
+    return B.KdProblem(T, d, V, K, chunk, dtype, tau)
+
+
+def ws_size(lib, p, op):
+    n = ctypes.c_size_t(0)
+    st = lib.kd_topk_kl_workspace_size(ctypes.byref(p), op, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), B.KD_ERR_SHAPE), (dict(d=0), B.KD_ERR_SHAPE), (dict(V=0), B.KD_ERR_SHAPE),
+    (dict(K=0), B.KD_ERR_SHAPE), (dict(K=1001), B.KD_ERR_SHAPE), (dict(chunk=-2), B.KD_ERR_SHAPE),
+    (dict(tau=0.0), B.KD_ERR_VALUE), (dict(tau=-1.0), B.KD_ERR_VALUE), (dict(tau=float("nan")), B.KD_ERR_VALUE),
+    (dict(tau=float("inf")), B.KD_ERR_VALUE), (dict(dtype=7), B.KD_ERR_UNSUPPORTED),
+    (dict(d=60), B.KD_ERR_UNSUPPORTED), (dict(K=1025, V=5000), B.KD_ERR_UNSUPPORTED),
+])
+def test_problem_validation(lib, kw, status):
+    st, _ = ws_size(lib, prob(**kw), B.KD_OP_FUSED)
+    assert st == status
+
+
+def test_size_limit_rejected(lib):
+    # W beyond the 2^31-byte operand limit
+    st, _ = ws_size(lib, prob(d=8192, V=200000, K=10, dtype=B.KD_F32), B.KD_OP_FUSED)
+    assert st == B.KD_ERR_UNSUPPORTED
+
+
+def test_workspace_independent_of_T(lib):
+    sizes = set()
+    for T in (1, 4096, 32768, 262144):
+        st, n = ws_size(lib, prob(T=T, d=2880, V=201088, K=100, chunk=2048), B.KD_OP_FUSED)
+        assert st == B.KD_OK
+        sizes.add(n)
+    assert len(sizes) == 1
+    (n,) = sizes
+    # G chunk (C x V_pad bf16) dominates; far below the T x V logits
+    assert 2048 * 201216 * 2 <= n < 2 * 2048 * 201216 * 2 + 64 * 2**20
+
+
+def test_workspace_by_op(lib):
+    p = prob(T=1000, d=256, V=4096, K=16, chunk=128)
+    f = ws_size(lib, p, B.KD_OP_FORWARD)[1]
+    b = ws_size(lib, p, B.KD_OP_BACKWARD)[1]
+    u = ws_size(lib, p, B.KD_OP_FUSED)[1]
+    assert 0 < f < u and 0 < b <= u
+    assert ws_size(lib, p, 9)[0] == B.KD_ERR_VALUE
+    assert lib.kd_topk_kl_workspace_size(ctypes.byref(p), 0, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_kl_workspace_size(None, 0, ctypes.byref(ctypes.c_size_t())) == B.KD_ERR_NULL
+
+
+def test_default_chunk(lib):
+    assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=201088, K=100))) == 4096
+    assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(K=0))) == 0
+    c = lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=2000000, K=100)))
+    assert 256 <= c < 4096 and c % 256 == 0
+
+
+def call_fwd(lib, p, H=P16, W=P16b, idx=P4, lg=P4, ig=None, loss=P4, lse=P4, rl=None, ws=P16, wsb=1 << 40):
+    return lib.kd_topk_kl_forward(ctypes.byref(p), H, W, idx, lg, ig, loss, lse, rl, ws, wsb, None)
+
+
+def call_bwd(lib, p, H=P16, W=P16b, idx=P4, lg=P4, ig=None, lse=P4, g=None, gH=P16, gW=P16b, ws=P16, wsb=1 << 40):
+    return lib.kd_topk_kl_backward(ctypes.byref(p), H, W, idx, lg, ig, lse, g, gH, gW, ws, wsb, None)
+
+
+def call_fused(lib, p, H=P16, W=P16b, idx=P4, lg=P4, ig=None, g=None, loss=P4, lse=None, rl=None, gH=P16, gW=P16b,
+               ws=P16, wsb=1 << 40):
+    return lib.kd_topk_kl_fused(ctypes.byref(p), H, W, idx, lg, ig, g, loss, lse, rl, gH, gW, ws, wsb, None)
+
+
+def test_forward_argument_errors(lib):
+    p = prob()
+    assert call_fwd(lib, p, H=None) == B.KD_ERR_NULL
+    assert call_fwd(lib, p, W=None) == B.KD_ERR_NULL
+    assert call_fwd(lib, p, idx=None) == B.KD_ERR_NULL
+    assert call_fwd(lib, p, lg=None) == B.KD_ERR_NULL
+    assert call_fwd(lib, p, loss=None) == B.KD_ERR_NULL
+    assert call_fwd(lib, p, lse=None) == B.KD_ERR_NULL
+    assert call_fwd(lib, p, ws=None) == B.KD_ERR_NULL
+    assert call_fwd(lib, p, H=MIS) == B.KD_ERR_ALIGN
+    assert call_fwd(lib, p, W=P4) == B.KD_ERR_ALIGN
+    assert call_fwd(lib, p, idx=MIS) == B.KD_ERR_ALIGN
+    assert call_fwd(lib, p, lse=MIS) == B.KD_ERR_ALIGN
+    assert call_fwd(lib, p, wsb=16) == B.KD_ERR_WORKSPACE
+    assert call_fwd(lib, prob(K=2000)) == B.KD_ERR_SHAPE
+    assert lib.kd_topk_kl_forward(None, P16, P16b, P4, P4, None, P4, P4, None, P16, 1 << 40, None) == B.KD_ERR_NULL
+
+
+def test_backward_argument_errors(lib):
+    p = prob()
+    assert call_bwd(lib, p, lse=None) == B.KD_ERR_NULL
+    assert call_bwd(lib, p, gH=None) == B.KD_ERR_NULL
+    assert call_bwd(lib, p, gW=None) == B.KD_ERR_NULL
+    assert call_bwd(lib, p, gH=P4) == B.KD_ERR_ALIGN
+    assert call_bwd(lib, p, gW=P4) == B.KD_ERR_ALIGN
+    assert call_bwd(lib, p, g=MIS) == B.KD_ERR_ALIGN
+    assert call_bwd(lib, p, wsb=0) == B.KD_ERR_WORKSPACE
+    assert call_bwd(lib, prob(tau=0.0)) == B.KD_ERR_VALUE
+
+
+def test_fused_argument_errors(lib):
+    p = prob()
+    assert call_fused(lib, p, loss=None) == B.KD_ERR_NULL
+    assert call_fused(lib, p, gW=None) == B.KD_ERR_NULL
+    assert call_fused(lib, p, gH=None) == B.KD_ERR_NULL
+    assert call_fused(lib, p, lse=MIS) == B.KD_ERR_ALIGN
+    assert call_fused(lib, p, rl=MIS) == B.KD_ERR_ALIGN
+    assert call_fused(lib, p, ws=P4) == B.KD_ERR_ALIGN
+    assert call_fused(lib, p, wsb=100) == B.KD_ERR_WORKSPACE
+    assert call_fused(lib, prob(d=12)) == B.KD_ERR_UNSUPPORTED
+
+
+def test_validate_argument_errors(lib):
+    p = prob()
+    assert lib.kd_topk_kl_validate(ctypes.byref(p), P4, P4, None, None, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_kl_validate(ctypes.byref(p), None, P4, None, P16, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_kl_validate(ctypes.byref(p), P4, P4, None, P4, None) == B.KD_ERR_ALIGN
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        msg = lib.kd_status_string(s).decode()
+        assert msg and msg != "unknown status"
+    assert lib.kd_status_string(99).decode() == "unknown status"
