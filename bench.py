@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked top-K KL loss (forward + backward) on one MI355X.
+
+One step = one call of the fused entry point over every position of the
+workload (logits GEMM, row kernel, grad_H GEMM and grad_W GEMM for each chunk),
+with inputs, outputs and workspace resident in HBM before the timed region.
+Prints one JSON line.  The default workload is the GPT-OSS-20B-like shape
+(T = 32768 positions, d = 2880, V = 201088, K = 100, bf16).
+
+Timing: W untimed warmup steps, then K steps bracketed by device
+synchronisation; per-kernel launch durations come from HIP events that the
+library records around each launch of every stage on the launch stream
+(kd_topk_kl_set_stage_events), over the same timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "fwd+bwd tokens/s of fused top-K KL loss; MFMA util % of bf16 peak; peak HBM GiB"
+KERNEL_SOURCES = ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp", "kd_topk_kl.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "chunked_top_kl_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw HIP events from the runtime the process already loaded (torch's)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.rt.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            arr[i] = e.value
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for e in arr:
+            self.rt.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(x, rows: int) -> dict:
+    """The fp64 oracle on the first `rows` positions of the same workload (fwd + both grads)."""
+    from oracle import kd_oracle
+
+    sel = slice(0, rows)
+    t0 = time.perf_counter()
+    kd_oracle.full(x.H[sel], x.W, x.topk_idx[sel], x.topk_logit[sel], x.ignore[sel], tau=x.tau)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": kd_oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {rows} positions of the workload, full vocabulary, fwd + grad_H + grad_W, "
+                      f"fp64, {dt:.1f} s"}
+
+
+def main() -> int:
+    from chunked_top_kl_head_amd import synth
+
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gptoss20b", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--chunk", type=int, default=0, help="rows per chunk (0 = the workload's)")
+    ap.add_argument("--mode", default="fused", choices=["fused", "split"],
+                    help="fused entry, or forward followed by backward")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the loss on a single GPU; positions shard naturally across GPUs "
+              "but no multi-GPU path is built. Run with --gpus 1.", file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from chunked_top_kl_head_amd import binding as B
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.WORKLOADS[args.workload]
+    chunk = args.chunk or wl.chunk
+    t_gen = time.perf_counter()
+    x = synth.workload_inputs(args.workload)
+    gen_s = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    if x.dtype == "bf16":
+        H = torch.from_numpy(x.H_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(x.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        H = torch.from_numpy(x.H).to(dev)
+        W = torch.from_numpy(x.W).to(dev)
+    idx = torch.from_numpy(x.topk_idx).to(dev)
+    lg = torch.from_numpy(x.topk_logit).to(dev)
+    ig = torch.from_numpy(x.ignore).to(dev) if x.ignore.any() else None
+    T, d, V, K = x.T, x.d, x.V, x.K
+
+    prob = B.problem(T, d, V, K, x.tau, H.dtype, chunk)
+    op = B.KD_OP_FUSED if args.mode == "fused" else B.KD_OP_BACKWARD
+    ws_bytes = B.workspace_size(prob, op)
+    if args.mode == "split":
+        ws_bytes = max(ws_bytes, B.workspace_size(prob, B.KD_OP_FORWARD))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    gH = torch.empty_like(H)
+    gW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+
+    def step():
+        if args.mode == "fused":
+            B.kd_topk_kl_fused(H, W, idx, lg, ig, temperature=x.tau, chunk=chunk, workspace=ws,
+                               grad_H=gH, grad_W=gW, loss=loss)
+        else:
+            l, s, _ = B.kd_topk_kl_forward(H, W, idx, lg, ig, temperature=x.tau, chunk=chunk, workspace=ws)
+            B.kd_topk_kl_backward(H, W, idx, lg, s, ig, temperature=x.tau, chunk=chunk, workspace=ws,
+                                  grad_H=gH, grad_W=gW)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-stage launch events over the timed steps
+    lib = B.load_library()
+    ev = HipEvents()
+    nchunks = (T + chunk - 1) // chunk
+    passes = 2 if args.mode == "split" else 1     # logits and rows run in both forward and backward
+    cap = args.steps * nchunks * passes
+    tables = []
+    for st in range(4):
+        b, e = ev.create(cap), ev.create(cap)
+        cnt = ctypes.c_int(0)
+        B._check("kd_topk_kl_set_stage_events", lib.kd_topk_kl_set_stage_events(st, b, e, cap, ctypes.byref(cnt)))
+        tables.append((b, e, cnt))
+    whole = ev.create(2)
+    stream = torch.cuda.current_stream()
+    torch.cuda.reset_peak_memory_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.rt.hipEventRecord(ctypes.c_void_p(whole[0]), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        step()
+    ev.rt.hipEventRecord(ctypes.c_void_p(whole[1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for st in range(4):
+        lib.kd_topk_kl_set_stage_events(st, None, None, 0, None)
+    peak_gib = torch.cuda.max_memory_allocated() / 2**30
+    gpu_ms = ev.elapsed_ms(whole[0], whole[1])
+    ms_per_step = gpu_ms / args.steps
+
+    # per-stage durations
+    stages = {}
+    rows_full = min(chunk, T)
+    for st, (b, e, cnt) in enumerate(tables):
+        n = cnt.value
+        durs = [ev.elapsed_ms(b[i], e[i]) for i in range(n)]
+        stages[B.STAGE_NAMES[st]] = dict(launches=n, avg_ms=(sum(durs) / n if n else 0.0),
+                                         total_ms_per_step=sum(durs) / args.steps)
+        ev.destroy(b)
+        ev.destroy(e)
+    ev.destroy(whole)
+    dom = max(stages, key=lambda k: stages[k]["total_ms_per_step"])
+    flops_step = 6.0 * T * d * V
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    # algorithmic work of one launch of the dominant stage: a full chunk of rows
+    if dom in ("logits", "grad_H", "grad_W"):
+        per_launch = 2.0 * rows_full * d * V
+        achieved = per_launch / (stages[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        # row kernel: reads and rewrites the chunk's G rows, reads partials
+        per_launch = rows_full * (2.0 * 2 * ((V + 255) // 256 * 256) + 8.0 * ((V + 255) // 256))
+        achieved = per_launch / (stages[dom]["avg_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tr = json.load(fh)
+        ent = tr.get(args.workload, {}).get(dom)
+        if ent and ent.get("source_sha") == kernel_source_hash() and ent.get("chunk") == chunk:
+            roof["traffic"] = ent["bytes_per_launch"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(T * args.steps / (gpu_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x.dtype,
+        "data": "synthetic (seeded H, W, Zipf(1.1) top-K ids, 3*Gumbel teacher logits)",
+        "config": {"workload": f"{wl.name}: T={T} d={d} V={V} K={K} tau={x.tau} {x.dtype}"
+                               + (f" mask={wl.mask[0]}" if wl.mask else ""),
+                   "chunk": chunk, "mode": args.mode, "positions": T, "kept": int(x.N),
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "mfma_util_pct": round(100.0 * tflops / peak, 2),
+        "peak_hbm_gib": round(peak_gib, 3),
+        "wall_s": round(wall, 3),
+        "stages": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in stages.items()},
+        "roofline": roof,
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, min(args.cpu_rows, T))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

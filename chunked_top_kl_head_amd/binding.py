@@ -29,8 +29,11 @@ EXPORTS = (
     "kd_topk_kl_backward",
     "kd_topk_kl_fused",
     "kd_topk_kl_validate",
+    "kd_topk_kl_set_stage_events",
     "kd_status_string",
 )
+KD_STAGE_LOGITS, KD_STAGE_ROWS, KD_STAGE_GRAD_H, KD_STAGE_GRAD_W = 0, 1, 2, 3
+STAGE_NAMES = ("logits", "rows", "grad_H", "grad_W")
 
 
 class KdProblem(ctypes.Structure):
@@ -70,6 +73,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kd_topk_kl_fused.restype = ctypes.c_int
     lib.kd_topk_kl_validate.argtypes = [prob, vp, vp, vp, vp, vp]
     lib.kd_topk_kl_validate.restype = ctypes.c_int
+    lib.kd_topk_kl_set_stage_events.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.kd_topk_kl_set_stage_events.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
     if path is None:

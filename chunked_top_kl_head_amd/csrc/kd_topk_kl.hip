@@ -46,6 +46,30 @@ struct Plan {
     size_t off_hdr, off_closs, off_stats, off_G, off_part, total;
 };
 
+// Optional event tables of the profiling hook (kd_topk_kl_set_stage_events).
+struct StageEvents {
+    void* const* begin = nullptr;
+    void* const* end = nullptr;
+    int capacity = 0;
+    int* recorded = nullptr;
+};
+static StageEvents g_stage_events[KD_NUM_STAGES];
+
+struct StageScope {
+    StageEvents& ev;
+    hipStream_t stream;
+    int slot;
+    StageScope(int stage, hipStream_t s) : ev(g_stage_events[stage]), stream(s), slot(-1) {
+        if (ev.begin && *ev.recorded < ev.capacity) {
+            slot = (*ev.recorded)++;
+            (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev.begin[slot]), stream);
+        }
+    }
+    ~StageScope() {
+        if (slot >= 0) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev.end[slot]), stream);
+    }
+};
+
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -53,7 +77,7 @@ static int64_t default_chunk(int64_t d, int64_t V, int es) {
     (void)d;
     const int64_t V_pad = cdiv(V, BM) * BM;
     int64_t C = 4096;
-    while (C > 256 && C * V_pad * es >= kOperandLimit) C -= 256;
+    while (C > 256 && (C + BN) * V_pad * es >= kOperandLimit) C -= 256;
     return C;
 }
 
@@ -91,9 +115,10 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
     q.V_pad = cdiv(q.V, BM) * BM;
     q.nvt = q.V_pad / BM;
     q.C = p->chunk > 0 ? p->chunk : default_chunk(q.d, q.V, q.es);
-    // operand extents addressed with 32-bit buffer offsets
-    if (q.V * q.d * q.es >= kOperandLimit || q.C * q.V_pad * q.es >= kOperandLimit ||
-        q.C * q.d * q.es >= kOperandLimit || q.C > (1 << 24))
+    // Operands are addressed with 32-bit buffer offsets; a tile may overhang an
+    // operand's end by up to one tile, and every such offset must stay below 2^31.
+    if ((q.V_pad + BM) * q.d * q.es >= kOperandLimit || (q.C + BN) * q.V_pad * q.es >= kOperandLimit ||
+        (q.C + BN) * q.d * q.es >= kOperandLimit || q.C > (1 << 24))
         return KD_ERR_UNSUPPORTED;
     const int bk = 128 / q.es;
     q.splits = choose_splits(cdiv(q.d, BM) * cdiv(q.C, BN), q.V_pad, bk);
@@ -161,6 +186,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
         const char* Hc = static_cast<const char*>(H) + t0 * pl.d * es;
         // ---- logits GEMM: Z^T = W H_c^T (M = V_pad, N = rc, K = d)
         {
+            StageScope scope(KD_STAGE_LOGITS, stream);
             const Operand A = operand(W, pl.d, pl.V * pl.d * es);
             const Operand B = operand(Hc, pl.d, rc * pl.d * es);
             const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk, 1);
@@ -187,11 +213,14 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.ignore = ignore;
             rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss;
             rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
-            hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), (size_t)(pl.nvt * sizeof(float)),
-                               stream, rp);
+            {
+                StageScope scope(KD_STAGE_ROWS, stream);
+                hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), (size_t)(pl.nvt * sizeof(float)),
+                                   stream, rp);
+            }
+            if (want_loss)
+                hipLaunchKernelGGL(loss_chunk_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, closs, (int)rc);
         }
-        if (want_loss)
-            hipLaunchKernelGGL(loss_chunk_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, closs, (int)rc);
         if (!want_grads) continue;
         // ---- grad_H^T = W^T G^T (M = d, N = rc, K = V_pad)
         {
@@ -202,8 +231,11 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             hp.out = static_cast<char*>(grad_H) + t0 * pl.d * es;
             hp.partial = part; hp.d = (int)pl.d; hp.rows = (int)rc; hp.C = (int)pl.C;
             hp.direct = pl.splits == 1;
-            hipLaunchKernelGGL((gemm_kernel<E, false, true, GradHEpi<E, BM, BN>>), gemm_grid(g, pl.splits),
-                               dim3(kThreads), 0, stream, A, B, g, hp);
+            {
+                StageScope scope(KD_STAGE_GRAD_H, stream);
+                hipLaunchKernelGGL((gemm_kernel<E, false, true, GradHEpi<E, BM, BN>>), gemm_grid(g, pl.splits),
+                                   dim3(kThreads), 0, stream, A, B, g, hp);
+            }
             if (pl.splits > 1) {
                 const int64_t n4 = rc * pl.d / 4;
                 const unsigned blocks = (unsigned)(cdiv(n4, kThreads) < 2048 ? cdiv(n4, kThreads) : 2048);
@@ -213,6 +245,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
         }
         // ---- grad_W^T (+)= H_c^T G (M = d, N = V_pad, K = rc)
         {
+            StageScope scope(KD_STAGE_GRAD_W, stream);
             const Operand A = operand(Hc, pl.d, rc * pl.d * es);
             const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
             const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 0);
@@ -349,6 +382,23 @@ kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx, c
     } catch (...) {
         return KD_ERR_INTERNAL;
     }
+}
+
+kd_status kd_topk_kl_set_stage_events(int stage, void* const* begin, void* const* end, int capacity,
+                                      int* recorded) {
+    if (stage < 0 || stage >= KD_NUM_STAGES) return KD_ERR_VALUE;
+    StageEvents& ev = g_stage_events[stage];
+    if (begin == nullptr) {
+        ev = StageEvents{};
+        return KD_OK;
+    }
+    if (!end || !recorded) return KD_ERR_NULL;
+    if (capacity < 0) return KD_ERR_VALUE;
+    ev.begin = begin;
+    ev.end = end;
+    ev.capacity = capacity;
+    ev.recorded = recorded;
+    return KD_OK;
 }
 
 const char* kd_status_string(kd_status status) {

@@ -142,6 +142,25 @@ kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx,
                               const float* topk_logit, const uint8_t* ignore,
                               int64_t* bad_count, void* stream);
 
+/* Kernel stages of every call, for timing. */
+typedef enum {
+    KD_STAGE_LOGITS = 0,   /* logits GEMM of a chunk (with its softmax-statistics epilogue) */
+    KD_STAGE_ROWS = 1,     /* per-row kernel of a chunk (lse, teacher, gather, loss, G) */
+    KD_STAGE_GRAD_H = 2,   /* grad_H GEMM of a chunk (its split reduction is not included) */
+    KD_STAGE_GRAD_W = 3,   /* grad_W GEMM of a chunk */
+    KD_NUM_STAGES = 4
+} kd_stage;
+
+/* Profiling hook.  While a table is installed for `stage`, the library
+ * brackets each launch of that stage with hipEventRecord(begin[i]) and
+ * hipEventRecord(end[i]) on the launch stream, for i = *recorded, *recorded+1,
+ * ... below `capacity`, incrementing the host counter *recorded at enqueue
+ * time.  The events (hipEvent_t) are created and owned by the caller.
+ * begin == NULL removes the table.  The tables are process-wide and not
+ * synchronised: install them only while no other thread calls the library. */
+kd_status kd_topk_kl_set_stage_events(int stage, void* const* begin, void* const* end, int capacity,
+                                      int* recorded);
+
 /* Static description of a status code. */
 const char* kd_status_string(kd_status status);
 
