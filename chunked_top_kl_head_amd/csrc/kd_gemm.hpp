@@ -2,7 +2,7 @@
 //
 // Computes a BM x BN output tile  D[m, n] = sum_k A[m, k] B[k, n]  per
 // workgroup of 256 threads (2 x 2 waves, each owning a (BM/2) x (BN/2) block
-// of 16 x 16 MFMA accumulators), then hands the fp32 accumulators to an
+// of 32 x 32 MFMA accumulators), then hands the fp32 accumulators to an
 // epilogue functor.  The three contractions of the loss are instances:
 //   logits   Z^T = W  H_c^T   (M = vocab, N = rows, K = hidden)  both operands K-contiguous
 //   grad_H   dH^T = W^T G^T   (M = hidden, N = rows, K = vocab)  A hidden-contiguous, B K-contiguous
@@ -11,18 +11,25 @@
 // M-indices of one N column: the stores of all three epilogues are then 8- or
 // 16-byte vectors along the contiguous dimension of the destination.
 //
+// bf16 uses v_mfma_f32_32x32x16_bf16 (the gfx950 shape that sustains the
+// dense bf16 rate); fp32 uses v_mfma_f32_32x32x2f32.
+//
 // Operands reach LDS through registers.  K-contiguous operands are copied as
 // 16-byte chunks; MN-contiguous operands are loaded as 16-byte vectors along
 // M, transposed in registers (8 x 8 for bf16, 4 x 4 for fp32) and stored as
-// K-contiguous chunks, so the MFMA fragment reads are always one ds_read_b128
-// per lane.  Tiles are double buffered in LDS with one barrier per K step.
-// Raw buffer loads return zero outside each operand's extent, which handles
-// all M/N/K tails without branches.
+// K-contiguous chunks, so every MFMA fragment read is one ds_read_b128 per
+// lane.  Tiles are double buffered in LDS with one barrier per K step; the
+// per-thread offsets of all loads are loop invariant and the K position costs
+// one add per load.  Raw buffer loads return zero outside each operand's
+// extent, which handles the M/N tails; the K tail of the last step masks
+// offsets explicitly.
 #pragma once
 
 #include "kd_common.hpp"
 
 namespace kd {
+
+typedef __attribute__((address_space(3))) char lds_t;
 
 template <typename E> struct Elem;
 template <> struct Elem<bf16_t> { static constexpr int size = 2; };
@@ -41,6 +48,17 @@ struct GemmGeom {
     int n_fastest;        // 1: consecutive tiles walk N (share the A tile), 0: walk M
 };
 
+__device__ __forceinline__ u32x4 lds_read16(const lds_t* base, int off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
+}
+__device__ __forceinline__ void lds_write16(lds_t* base, int off, u32x4 v) {
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base + off) = v;
+}
+
+__device__ __forceinline__ u32x4 buf_load16_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Global -> register -> LDS loaders for a ROWS x 128-byte operand tile
 // ---------------------------------------------------------------------------
@@ -53,8 +71,7 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, true> {
     static constexpr int EPC = 16 / ES;          // elements per chunk
     static constexpr int NCH = ROWS / 32;        // chunks per thread
     __amdgpu_buffer_rsrc_t rs;
-    uint32_t off0;       // byte offset of this thread's first chunk at k = 0
-    uint32_t row_bytes;  // ld * ES
+    uint32_t voff[NCH];
     int c, r0;
     u32x4 reg[NCH];
 
@@ -62,21 +79,22 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, true> {
         rs = make_rsrc(op.ptr, op.bytes);
         c = tid & 7;
         r0 = tid >> 3;
-        row_bytes = (uint32_t)(op.ld * ES);
-        off0 = (uint32_t)(((int64_t)(m0 + r0) * op.ld + c * EPC) * ES);
-    }
-    __device__ __forceinline__ void load(int k0, int kend) {
-        const bool ok = (k0 + c * EPC) < kend;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            uint32_t o = off0 + (uint32_t)(32 * i) * row_bytes + (uint32_t)(k0 * ES);
-            reg[i] = buf_load16(rs, ok ? o : kOOB);
-        }
-    }
-    __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
         for (int i = 0; i < NCH; ++i)
-            *reinterpret_cast<u32x4*>(lds + lds_off(r0 + 32 * i, c)) = reg[i];
+            voff[i] = (uint32_t)(((int64_t)(m0 + r0 + 32 * i) * op.ld + c * EPC) * ES);
+    }
+    // k0: first K element of the step; full: the whole step lies below kend.
+    // The whole byte offset travels in the vector offset (the bounds check
+    // then covers it); the scalar offset stays 0.
+    __device__ __forceinline__ void load(int k0, int kend, bool full) {
+        const uint32_t koff = (uint32_t)(k0 * ES);
+        const bool ok = full || (k0 + c * EPC) < kend;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) reg[i] = buf_load16_s(rs, ok ? voff[i] + koff : kOOB, 0u);
+    }
+    __device__ __forceinline__ void store(lds_t* lds) const {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) lds_write16(lds, lds_off(r0 + 32 * i, c), reg[i]);
     }
 };
 
@@ -89,11 +107,11 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, false> {
     static constexpr int MB = ROWS / EPC;        // m-blocks per tile
     static constexpr int NBLK = 8 * MB;          // 8 k-chunks per 128-byte row
     static constexpr int BPT = (NBLK + kThreads - 1) / kThreads;
+    static_assert(NBLK % kThreads == 0, "every thread owns whole blocks");
     __amdgpu_buffer_rsrc_t rs;
     uint32_t boff[BPT];  // byte offset of block i at k = 0
     uint32_t k_bytes;    // ld * ES (one k step)
     int mb[BPT], kc[BPT];
-    bool live[BPT];
     u32x4 reg[BPT][EPC];
 
     __device__ __forceinline__ void init(const Operand& op, int m0, int tid) {
@@ -102,27 +120,26 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, false> {
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             const int b = tid + kThreads * i;
-            live[i] = b < NBLK;
             mb[i] = b % MB;
             kc[i] = b / MB;
             boff[i] = (uint32_t)(((int64_t)kc[i] * EPC * op.ld + m0 + mb[i] * EPC) * ES);
         }
     }
-    __device__ __forceinline__ void load(int k0, int kend) {
+    __device__ __forceinline__ void load(int k0, int kend, bool full) {
+        const uint32_t koff = (uint32_t)k0 * k_bytes;
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) {
-                const int k = k0 + kc[i] * EPC + e;
-                const uint32_t o = boff[i] + (uint32_t)(k0 + e) * k_bytes;
-                reg[i][e] = buf_load16(rs, (live[i] && k < kend) ? o : kOOB);
+                const uint32_t vo = boff[i] + (uint32_t)e * k_bytes + koff;
+                const bool ok = full || (k0 + kc[i] * EPC + e) < kend;
+                reg[i][e] = buf_load16_s(rs, ok ? vo : kOOB, 0u);
             }
         }
     }
-    __device__ __forceinline__ void store(char* lds) const {
+    __device__ __forceinline__ void store(lds_t* lds) const {
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            if (!live[i]) continue;
             if constexpr (EPC == 8) {
                 // 8 x 8 transpose of 16-bit elements: out[mm] holds k = 0..7 of column mm.
 #pragma unroll
@@ -135,13 +152,13 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, false> {
                         o[j] = (mm & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u))
                                         : ((lo & 0xFFFFu) | (hi << 16));
                     }
-                    *reinterpret_cast<u32x4*>(lds + lds_off(mb[i] * 8 + mm, kc[i])) = o;
+                    lds_write16(lds, lds_off(mb[i] * 8 + mm, kc[i]), o);
                 }
             } else {
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm) {
                     u32x4 o = {reg[i][0][mm], reg[i][1][mm], reg[i][2][mm], reg[i][3][mm]};
-                    *reinterpret_cast<u32x4*>(lds + lds_off(mb[i] * 4 + mm, kc[i])) = o;
+                    lds_write16(lds, lds_off(mb[i] * 4 + mm, kc[i]), o);
                 }
             }
         }
@@ -149,53 +166,72 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, false> {
 };
 
 // ---------------------------------------------------------------------------
-// MFMA accumulator block of one wave
+// MFMA accumulator block of one wave: (BM/2) x (BN/2) as 32 x 32 fragments.
+// Lane l of fragment (i, j) holds tile rows  wm*BM/2 + 32 i + 8 q + 4 (l >> 5) + r
+// (accumulator element 4 q + r, q, r in 0..3) of tile column  wn*BN/2 + 32 j + (l & 31).
 // ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
 template <typename E, int BM, int BN> struct WaveMma {
-    static constexpr int FM = BM / 32;   // 16-row fragments per wave (wave covers BM/2 rows)
-    static constexpr int FN = BN / 32;
-    f32x4 acc[FM][FN];
+    static constexpr int FM = BM / 64;   // 32-row fragments per wave (wave covers BM/2 rows)
+    static constexpr int FN = BN / 64;
+    f32x16 acc[FM][FN];
 
     __device__ __forceinline__ void zero() {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     }
 
-    // One 128-byte K slab: two halves of four 16-byte chunks each.
-    __device__ __forceinline__ void step(const char* la, const char* lb, int wm, int wn, int lane) {
-        const int lr = lane & 15, lc = lane >> 4;
+    // One 128-byte K slab: four sub-steps of two 16-byte chunks each.  Lanes
+    // 0..31 read chunk 2s, lanes 32..63 chunk 2s + 1 of their row.
+    __device__ __forceinline__ void step(const lds_t* la, const lds_t* lb, int wm, int wn, int lane) {
+        const int lr = lane & 31, lc = lane >> 5;
+        u32x4 a[2][FM], b[2][FN];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            u32x4 a[FM], b[FN];
+        for (int i = 0; i < FM; ++i) a[0][i] = lds_read16(la, lds_off(wm * (BM / 2) + i * 32 + lr, lc));
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                a[i] = *reinterpret_cast<const u32x4*>(la + lds_off(wm * (BM / 2) + i * 16 + lr, 4 * h + lc));
+        for (int j = 0; j < FN; ++j) b[0][j] = lds_read16(lb, lds_off(wn * (BN / 2) + j * 32 + lr, lc));
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                b[j] = *reinterpret_cast<const u32x4*>(lb + lds_off(wn * (BN / 2) + j * 16 + lr, 4 * h + lc));
+        for (int s = 0; s < 4; ++s) {
+            const int cur = s & 1;
+            if (s + 1 < 4) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    a[cur ^ 1][i] = lds_read16(la, lds_off(wm * (BM / 2) + i * 32 + lr, 2 * (s + 1) + lc));
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    b[cur ^ 1][j] = lds_read16(lb, lds_off(wn * (BN / 2) + j * 32 + lr, 2 * (s + 1) + lc));
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     if constexpr (Elem<E>::size == 2) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]),
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, a[cur][i]), __builtin_bit_cast(bf16x8, b[cur][j]),
                             acc[i][j], 0, 0, 0);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                __uint_as_float(a[i][e]), __uint_as_float(b[j][e]), acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                __uint_as_float(a[cur][i][e]), __uint_as_float(b[cur][j][e]), acc[i][j], 0, 0, 0);
                     }
                 }
         }
     }
-};
 
-// Accumulator element (i, j, r) of lane `lane` in wave (wm, wn) sits at tile
-// row  wm*BM/2 + 16 i + 4 (lane >> 4) + r  and tile column  wn*BN/2 + 16 j + (lane & 15).
+    // tile coordinates of accumulator element (i, j, e) for lane `lane`
+    static __device__ __forceinline__ int row(int wm, int i, int q, int lane) {
+        return wm * (BM / 2) + 32 * i + 8 * q + 4 * (lane >> 5);
+    }
+    static __device__ __forceinline__ int col(int wn, int j, int lane) {
+        return wn * (BN / 2) + 32 * j + (lane & 31);
+    }
+};
 
 template <int BM, int BN>
 constexpr int gemm_lds_bytes() { return 2 * (BM + BN) * 128; }
@@ -205,7 +241,7 @@ constexpr int gemm_lds_bytes() { return 2 * (BM + BN) * 128; }
 // ---------------------------------------------------------------------------
 template <typename E, int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_body(const Operand& A, const Operand& B, const GemmGeom& g,
-                                          const typename Epi::Params& ep, char* smem) {
+                                          const typename Epi::Params& ep, lds_t* smem) {
     constexpr int ES = Elem<E>::size;
     constexpr int BK = 128 / ES;
     // XCD-aware remap: hardware dispatches workgroup b to XCD b % 8; give each
@@ -236,26 +272,29 @@ __device__ __forceinline__ void gemm_body(const Operand& A, const Operand& B, co
     WaveMma<E, BM, BN> mma;
     mma.zero();
 
-    char* stage[2] = {smem, smem + (BM + BN) * 128};
+    constexpr int kStage = (BM + BN) * 128;
     if (nk > 0) {
-        la.load(kbeg, kend);
-        lb.load(kbeg, kend);
-        la.store(stage[0]);
-        lb.store(stage[0] + BM * 128);
+        const bool full = kbeg + BK <= kend;
+        la.load(kbeg, kend, full);
+        lb.load(kbeg, kend, full);
+        la.store(smem);
+        lb.store(smem + BM * 128);
     }
     __syncthreads();
     for (int it = 0; it < nk; ++it) {
-        const int cur = it & 1;
+        lds_t* cur = smem + (it & 1) * kStage;
+        lds_t* nxt = smem + ((it & 1) ^ 1) * kStage;
         const bool more = it + 1 < nk;
         if (more) {
             const int k1 = kbeg + (it + 1) * BK;
-            la.load(k1, kend);
-            lb.load(k1, kend);
+            const bool full = k1 + BK <= kend;
+            la.load(k1, kend, full);
+            lb.load(k1, kend, full);
         }
-        mma.step(stage[cur], stage[cur] + BM * 128, wm, wn, lane);
+        mma.step(cur, cur + BM * 128, wm, wn, lane);
         if (more) {
-            la.store(stage[cur ^ 1]);
-            lb.store(stage[cur ^ 1] + BM * 128);
+            la.store(nxt);
+            lb.store(nxt + BM * 128);
         }
         __syncthreads();
     }

@@ -50,7 +50,8 @@ struct LogitsParams {
 
 template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
     using Params = LogitsParams;
-    static constexpr int FM = BM / 32, FN = BN / 32;
+    using Mma = WaveMma<E, BM, BN>;
+    static constexpr int FM = Mma::FM, FN = Mma::FN;
 
     static __device__ __forceinline__ void store4(const Params& p, int t, int v0, float x0, float x1,
                                                   float x2, float x3) {
@@ -63,69 +64,73 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
         }
     }
 
-    static __device__ __forceinline__ void apply(WaveMma<E, BM, BN>& mma, int m0, int n0, int /*split*/,
-                                                 int wm, int wn, int lane, int tid, char* smem,
-                                                 const Params& p) {
-        const int lr = lane & 15, lc = lane >> 4;
+    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int /*split*/, int wm, int wn,
+                                                 int lane, int tid, lds_t* smem, const Params& p) {
         // base-2 logits; ids at or beyond V are excluded (-inf)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool ok = (m0 + wm * (BM / 2) + 16 * i + 4 * lc + r) < p.V;
+            for (int q = 0; q < 4; ++q) {
+                const int v0 = m0 + Mma::row(wm, i, q, lane);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    mma.acc[i][j][r] = ok ? mma.acc[i][j][r] * p.scale2 : -INFINITY;
+                for (int r = 0; r < 4; ++r) {
+                    const bool ok = v0 + r < p.V;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        mma.acc[i][j][4 * q + r] = ok ? mma.acc[i][j][4 * q + r] * p.scale2 : -INFINITY;
+                }
             }
 
         if constexpr (MODE == kBwd) {
             const float s = p.hdr->s;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int t = n0 + wn * (BN / 2) + 16 * j + lr;
+                const int t = n0 + Mma::col(wn, j, lane);
                 if (t >= p.rows) continue;
                 const bool kept = (p.ignore == nullptr) || (p.ignore[t] == 0);
                 const float st = kept ? s : 0.f;
                 const float l2 = p.lse[t] * kLog2e;
 #pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    float g[4];
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) g[r] = st * fast_exp2(mma.acc[i][j][r] - l2);
-                    store4(p, t, m0 + wm * (BM / 2) + 16 * i + 4 * lc, g[0], g[1], g[2], g[3]);
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        float g[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) g[r] = st * fast_exp2(mma.acc[i][j][4 * q + r] - l2);
+                        store4(p, t, m0 + Mma::row(wm, i, q, lane), g[0], g[1], g[2], g[3]);
+                    }
             }
             return;
         } else {
-            float* red = reinterpret_cast<float*>(smem);   // [4][BN]: max of wm=0,1 then sum of wm=0,1
+            // [4][BN]: column max of wm = 0, 1, then column sum of wm = 0, 1
+            __attribute__((address_space(3))) float* red =
+                reinterpret_cast<__attribute__((address_space(3))) float*>(smem);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, mma.acc[i][j][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, mma.acc[i][j][e]);
                 mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-                if (lc == 0) red[wm * BN + wn * (BN / 2) + 16 * j + lr] = mx;
+                if (lane < 32) red[wm * BN + Mma::col(wn, j, lane)] = mx;
             }
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int n = wn * (BN / 2) + 16 * j + lr;
+                const int n = Mma::col(wn, j, lane);
                 const float M = fmaxf(red[n], red[BN + n]);
                 float s = 0.f;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float e = fast_exp2(mma.acc[i][j][r] - M);
-                        mma.acc[i][j][r] = e;
-                        s += e;
+                    for (int e = 0; e < 16; ++e) {
+                        const float x = fast_exp2(mma.acc[i][j][e] - M);
+                        mma.acc[i][j][e] = x;
+                        s += x;
                     }
-                s += __shfl_xor(s, 16, kWave);
                 s += __shfl_xor(s, 32, kWave);
-                if (lc == 0) red[(2 + wm) * BN + n] = s;
+                if (lane < 32) red[(2 + wm) * BN + n] = s;
             }
             __syncthreads();
             if (tid < BN) {
@@ -138,12 +143,14 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
             if constexpr (MODE == kFused) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const int t = n0 + wn * (BN / 2) + 16 * j + lr;
+                    const int t = n0 + Mma::col(wn, j, lane);
                     if (t >= p.rows) continue;
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
-                        store4(p, t, m0 + wm * (BM / 2) + 16 * i + 4 * lc, mma.acc[i][j][0],
-                               mma.acc[i][j][1], mma.acc[i][j][2], mma.acc[i][j][3]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            store4(p, t, m0 + Mma::row(wm, i, q, lane), mma.acc[i][j][4 * q],
+                                   mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]);
                 }
             }
         }
@@ -163,30 +170,33 @@ struct GradHParams {
 
 template <typename E, int BM, int BN> struct GradHEpi {
     using Params = GradHParams;
-    static constexpr int FM = BM / 32, FN = BN / 32;
-    static __device__ __forceinline__ void apply(WaveMma<E, BM, BN>& mma, int m0, int n0, int split,
-                                                 int wm, int wn, int lane, int, char*, const Params& p) {
-        const int lr = lane & 15, lc = lane >> 4;
+    using Mma = WaveMma<E, BM, BN>;
+    static constexpr int FM = Mma::FM, FN = Mma::FN;
+    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int split, int wm, int wn, int lane,
+                                                 int, lds_t*, const Params& p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int t = n0 + wn * (BN / 2) + 16 * j + lr;
+            const int t = n0 + Mma::col(wn, j, lane);
             if (t >= p.rows) continue;
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int h = m0 + wm * (BM / 2) + 16 * i + 4 * lc;
-                if (h >= p.d) continue;
-                const f32x4 v = mma.acc[i][j];
-                if (p.direct) {
-                    if constexpr (Elem<E>::size == 2) {
-                        u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)t * p.d + h) = w;
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int h = m0 + Mma::row(wm, i, q, lane);
+                    if (h >= p.d) continue;
+                    const f32x4 v = {mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
+                                     mma.acc[i][j][4 * q + 3]};
+                    if (p.direct) {
+                        if constexpr (Elem<E>::size == 2) {
+                            u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)t * p.d + h) = w;
+                        } else {
+                            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)t * p.d + h) = v;
+                        }
                     } else {
-                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)t * p.d + h) = v;
+                        *reinterpret_cast<f32x4*>(p.partial + ((int64_t)split * p.C + t) * p.d + h) = v;
                     }
-                } else {
-                    *reinterpret_cast<f32x4*>(p.partial + ((int64_t)split * p.C + t) * p.d + h) = v;
                 }
-            }
         }
     }
 };
@@ -203,23 +213,26 @@ struct GradWParams {
 
 template <typename E, int BM, int BN> struct GradWEpi {
     using Params = GradWParams;
-    static constexpr int FM = BM / 32, FN = BN / 32;
-    static __device__ __forceinline__ void apply(WaveMma<E, BM, BN>& mma, int m0, int n0, int,
-                                                 int wm, int wn, int lane, int, char*, const Params& p) {
-        const int lr = lane & 15, lc = lane >> 4;
+    using Mma = WaveMma<E, BM, BN>;
+    static constexpr int FM = Mma::FM, FN = Mma::FN;
+    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int,
+                                                 lds_t*, const Params& p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int v = n0 + wn * (BN / 2) + 16 * j + lr;
+            const int v = n0 + Mma::col(wn, j, lane);
             if (v >= p.V) continue;
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int h = m0 + wm * (BM / 2) + 16 * i + 4 * lc;
-                if (h >= p.d) continue;
-                f32x4* dst = reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h);
-                f32x4 val = mma.acc[i][j];
-                if (p.accumulate) val += *dst;
-                *dst = val;
-            }
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int h = m0 + Mma::row(wm, i, q, lane);
+                    if (h >= p.d) continue;
+                    f32x4* dst = reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h);
+                    f32x4 val = {mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
+                                 mma.acc[i][j][4 * q + 3]};
+                    if (p.accumulate) val += *dst;
+                    *dst = val;
+                }
         }
     }
 };

@@ -34,7 +34,7 @@ constexpr int64_t kOperandLimit = (int64_t)1 << 31;
 template <typename E, bool AK, bool BK, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(Operand A, Operand B, GemmGeom g, typename Epi::Params ep) {
     __shared__ __attribute__((aligned(16))) char smem[gemm_lds_bytes<BM, BN>()];
-    gemm_body<E, BM, BN, AK, BK, Epi>(A, B, g, ep, smem);
+    gemm_body<E, BM, BN, AK, BK, Epi>(A, B, g, ep, (lds_t*)smem);
 }
 
 struct Plan {
