@@ -13,7 +13,7 @@
 // the boundary are natural-log.
 #pragma once
 
-#include "kd_gemm.hpp"
+#include "kd_gemm_dtl.hpp"
 
 namespace kd {
 
@@ -50,8 +50,6 @@ struct LogitsParams {
 
 template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
     using Params = LogitsParams;
-    using Mma = WaveMma<E, BM, BN>;
-    static constexpr int FM = Mma::FM, FN = Mma::FN;
 
     static __device__ __forceinline__ void store4(const Params& p, int t, int v0, float x0, float x1,
                                                   float x2, float x3) {
@@ -64,8 +62,10 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
         }
     }
 
+    template <class Mma>
     static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int /*split*/, int wm, int wn,
                                                  int lane, int tid, lds_t* smem, const Params& p) {
+        constexpr int FM = Mma::FM, FN = Mma::FN;
         // base-2 logits; ids at or beyond V are excluded (-inf)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -170,10 +170,10 @@ struct GradHParams {
 
 template <typename E, int BM, int BN> struct GradHEpi {
     using Params = GradHParams;
-    using Mma = WaveMma<E, BM, BN>;
-    static constexpr int FM = Mma::FM, FN = Mma::FN;
+    template <class Mma>
     static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int split, int wm, int wn, int lane,
                                                  int, lds_t*, const Params& p) {
+        constexpr int FM = Mma::FM, FN = Mma::FN;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int t = n0 + Mma::col(wn, j, lane);
@@ -213,10 +213,10 @@ struct GradWParams {
 
 template <typename E, int BM, int BN> struct GradWEpi {
     using Params = GradWParams;
-    using Mma = WaveMma<E, BM, BN>;
-    static constexpr int FM = Mma::FM, FN = Mma::FN;
+    template <class Mma>
     static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int,
                                                  lds_t*, const Params& p) {
+        constexpr int FM = Mma::FM, FN = Mma::FN;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int v = n0 + Mma::col(wn, j, lane);

@@ -31,10 +31,29 @@ namespace kd {
 constexpr int BM = 256, BN = 256;      // output tile of every contraction
 constexpr int64_t kOperandLimit = (int64_t)1 << 31;
 
+// fp32 operands: register-staged engine (4 waves, 32x32x2 fp32 MFMA)
 template <typename E, bool AK, bool BK, class Epi>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(Operand A, Operand B, GemmGeom g, typename Epi::Params ep) {
     __shared__ __attribute__((aligned(16))) char smem[gemm_lds_bytes<BM, BN>()];
     gemm_body<E, BM, BN, AK, BK, Epi>(A, B, g, ep, (lds_t*)smem);
+}
+
+// bf16 operands: direct-to-LDS engine (8 waves, 32x32x16 bf16 MFMA)
+template <bool AK, bool BK, class Epi>
+__global__ __launch_bounds__(kDtlThreads) void gemm_kernel_dtl(Operand A, Operand B, GemmGeom g,
+                                                               typename Epi::Params ep) {
+    __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * 128];
+    gemm_body_dtl<BM, BN, AK, BK, Epi>(A, B, g, ep, (lds_t*)smem);
+}
+
+// Launch of one contraction on the engine that matches the element type.
+template <typename E, bool AK, bool BK, class Epi>
+static void launch_gemm(dim3 grid, hipStream_t stream, const Operand& A, const Operand& B, const GemmGeom& g,
+                        const typename Epi::Params& ep) {
+    if constexpr (Elem<E>::size == 2)
+        hipLaunchKernelGGL((gemm_kernel_dtl<AK, BK, Epi>), grid, dim3(kDtlThreads), 0, stream, A, B, g, ep);
+    else
+        hipLaunchKernelGGL((gemm_kernel<E, AK, BK, Epi>), grid, dim3(kThreads), 0, stream, A, B, g, ep);
 }
 
 struct Plan {
@@ -197,11 +216,11 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             lp.ignore = ignore ? ignore + t0 : nullptr;
             const dim3 grid = gemm_grid(g, 1);
             if (op == KD_OP_FORWARD)
-                hipLaunchKernelGGL((gemm_kernel<E, true, true, LogitsEpi<E, BM, BN, kStats>>), grid, dim3(kThreads), 0, stream, A, B, g, lp);
+                launch_gemm<E, true, true, LogitsEpi<E, BM, BN, kStats>>(grid, stream, A, B, g, lp);
             else if (op == KD_OP_FUSED)
-                hipLaunchKernelGGL((gemm_kernel<E, true, true, LogitsEpi<E, BM, BN, kFused>>), grid, dim3(kThreads), 0, stream, A, B, g, lp);
+                launch_gemm<E, true, true, LogitsEpi<E, BM, BN, kFused>>(grid, stream, A, B, g, lp);
             else
-                hipLaunchKernelGGL((gemm_kernel<E, true, true, LogitsEpi<E, BM, BN, kBwd>>), grid, dim3(kThreads), 0, stream, A, B, g, lp);
+                launch_gemm<E, true, true, LogitsEpi<E, BM, BN, kBwd>>(grid, stream, A, B, g, lp);
         }
         // ---- row kernel
         {
@@ -233,8 +252,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             hp.direct = pl.splits == 1;
             {
                 StageScope scope(KD_STAGE_GRAD_H, stream);
-                hipLaunchKernelGGL((gemm_kernel<E, false, true, GradHEpi<E, BM, BN>>), gemm_grid(g, pl.splits),
-                                   dim3(kThreads), 0, stream, A, B, g, hp);
+                launch_gemm<E, false, true, GradHEpi<E, BM, BN>>(gemm_grid(g, pl.splits), stream, A, B, g, hp);
             }
             if (pl.splits > 1) {
                 const int64_t n4 = rc * pl.d / 4;
@@ -251,8 +269,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 0);
             GradWParams wp{};
             wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0;
-            hipLaunchKernelGGL((gemm_kernel<E, false, false, GradWEpi<E, BM, BN>>), gemm_grid(g, 1), dim3(kThreads), 0,
-                               stream, A, B, g, wp);
+            launch_gemm<E, false, false, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp);
         }
     }
     if (want_loss) hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, stream, hdr, loss);
