@@ -10,14 +10,16 @@
 // (each lane's 16 bytes land at the wave's LDS base + 16 * lane; the global
 // address of every lane is chosen so that the LDS image is the swizzled tile).
 // Out-of-range lanes of a raw buffer write zeros, which handles every tail.
-//   K-contiguous operand: LDS tile [rows][BK] (128-byte rows, 16-byte chunks
-//     XOR-swizzled by row); fragments are one ds_read_b128 per lane.
+//   K-contiguous operand: LDS tile [rows][BK] (16-byte chunks XOR-swizzled by
+//     row); fragments are one ds_read_b128 per lane.
 //   MN-contiguous operand: LDS tile [BK][rows] in the operand's own layout
 //     (512-byte k-rows, 16-byte chunks XOR-swizzled by k); fragments are two
 //     ds_read_b64_tr_b16 per lane, which transpose 4 x 16 blocks across the
 //     16 lanes of a quarter-wave.
-// Two LDS stages of 64 KiB; each K step waits for its own loads, meets at one
-// barrier, issues the next step's loads, then runs 4 MFMA sub-steps.
+// kDtlStages LDS stages (one K step of kDtlBK each): all but one are in flight
+// while one is consumed; each step waits only for its own loads, meets at one
+// barrier, issues the step kDtlStages - 1 ahead, then runs kDtlBK / 16 MFMA
+// sub-steps.
 #pragma once
 
 #include "kd_gemm.hpp"
@@ -28,9 +30,28 @@ constexpr int kDtlThreads = 512;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
-__device__ __forceinline__ void dtl_load16(__amdgpu_buffer_rsrc_t r, lds_t* lds_wave_base, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
-                                             0, 0, 0);
+// Raw buffer descriptor as four dwords (gfx9: 48-bit base, stride 0,
+// num_records = bytes, 32-bit data format).
+__device__ __forceinline__ u32x4 rsrc_words(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// One direct-to-LDS load: lane l's 16 bytes at byte offset `voff` of the
+// buffer land at LDS byte address lds_addr + 16 l (out of range: zeros).  The
+// instruction has no destination register; it is issued from asm so that the
+// compiler does not add its own conservative vmcnt waits before unrelated LDS
+// reads.  Completion is awaited explicitly with s_waitcnt vmcnt(N) before the
+// barrier that publishes a stage.
+__device__ __forceinline__ void dtl_load16(const u32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const lds_t* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
 __device__ __forceinline__ u32x2 lds_read8_tr(const lds_t* base, int off) {
@@ -39,34 +60,67 @@ __device__ __forceinline__ u32x2 lds_read8_tr(const lds_t* base, int off) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-// MN-contiguous tile: byte offset of element (k, m) in a [64][256] bf16 tile.
+// K step of the engine (bf16 elements) and pipeline depth.  A stage holds the
+// A and B tiles of one step: 2 * 256 * kDtlBK * 2 bytes.
+#ifndef KD_DTL_BK
+#define KD_DTL_BK 64
+#endif
+#ifndef KD_DTL_STAGES
+#define KD_DTL_STAGES 2
+#endif
+constexpr int kDtlBK = KD_DTL_BK;
+constexpr int kDtlStages = KD_DTL_STAGES;
+constexpr int kDtlTile = 256 * kDtlBK * 2;   // bytes of one operand tile per step
+static_assert(kDtlBK == 32 || kDtlBK == 64, "K step");
+static_assert(kDtlStages >= 2 && kDtlStages * 2 * kDtlTile <= 160 * 1024, "stages fit in LDS");
+
+// K-contiguous tile of one step: [rows][kDtlBK] bf16, rows of kDtlBK / 8
+// 16-byte chunks.  Chunk c of row r is stored at c ^ k_swz(r), chosen so that
+// a fragment read (32 consecutive rows, one chunk) touches distinct banks
+// whether the LDS serves 8 lanes of a 16-byte read per cycle from 32 banks or
+// 16 lanes from 64 banks.
+constexpr int kRowBytes = kDtlBK * 2;
+__device__ __forceinline__ int k_swz(int r) {
+    if constexpr (kDtlBK == 64) return (r ^ (r >> 3)) & 7;
+    else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+__device__ __forceinline__ int k_off(int r, int c) {
+    return r * kRowBytes + ((c ^ k_swz(r)) << 4);
+}
+
+// MN-contiguous tile of one step: [kDtlBK][256] bf16, 512-byte k-rows of 32
+// chunks; chunk c of k-row k is stored at c ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 4).
+// A transposing read touches k-rows {k0..k0+3} (and k0+8.. in the other half
+// wave) x four consecutive chunks, which this places in distinct banks.
 __device__ __forceinline__ int mn_off(int k, int m) {
-    return (k << 9) + ((((m >> 3) ^ ((k & 3) << 1))) << 4) + ((m & 7) << 1);
+    return (k << 9) + (((m >> 3) ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 4)) << 4) + ((m & 7) << 1);
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS loaders of one 64-element K step (bf16) of a ROWS-row operand.
-// Every wave issues NI instructions of 1 KiB; instruction i of wave w fills
-// LDS kilobyte (w * NI + i) of the tile.
+// Direct-to-LDS loaders of one K step of a 256-row operand.  Every wave issues
+// NI instructions of 1 KiB; instruction i of wave w fills LDS kilobyte
+// w * NI + i of the tile.
 // ---------------------------------------------------------------------------
 template <int ROWS, bool KMAJOR> struct DtlLoader;
 
 template <int ROWS> struct DtlLoader<ROWS, true> {
-    static constexpr int NI = ROWS * 128 / 1024 / (kDtlThreads / 64);   // 4 for 256 rows
-    __amdgpu_buffer_rsrc_t rs;
+    static_assert(ROWS == 256, "tile rows");
+    static constexpr int NI = kDtlTile / 1024 / (kDtlThreads / 64);
+    static constexpr int RPK = 1024 / kRowBytes;                  // rows per kilobyte
+    static constexpr int CPR = kRowBytes / 16;                    // chunks per row
+    u32x4 rs;
     uint32_t voff[NI];
-    int lane_k;          // first element of this lane's chunk within the step
+    int kl[NI];          // element offset of this lane's chunk within the step
     int lds0;            // LDS byte offset of this wave's first kilobyte
 
     __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
-        rs = make_rsrc(op.ptr, op.bytes);
+        rs = rsrc_words(op.ptr, op.bytes);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int kb = wave * NI + i;              // kilobyte of the tile = 8 rows
-            const int r = kb * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);   // logical chunk stored at this lane's slot
+            const int r = (wave * NI + i) * RPK + lane / CPR;
+            const int c = (lane % CPR) ^ k_swz(r);                   // logical chunk at this lane's slot
+            kl[i] = c * 8;
             voff[i] = (uint32_t)(((int64_t)(m0 + r) * op.ld + c * 8) * 2);
-            if (i == 0) lane_k = c * 8;
         }
         lds0 = wave * NI * 1024;
     }
@@ -74,51 +128,43 @@ template <int ROWS> struct DtlLoader<ROWS, true> {
         const uint32_t koff = (uint32_t)(k0 * 2);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            // chunk index differs per instruction (row-dependent swizzle): recompute its k
-            bool ok = full;
-            if (!full) {
-                const int lane = (int)(threadIdx.x & 63);
-                const int r = ((int)(threadIdx.x >> 6) * NI + i) * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);
-                ok = (k0 + c * 8) < kend;
-            }
-            dtl_load16(rs, tile + lds0 + i * 1024, ok ? voff[i] + koff : kOOB);
+            const bool ok = full || (k0 + kl[i]) < kend;
+            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] + koff : kOOB);
         }
     }
     // fragment of 32 rows starting at row r0, sub-step s (k = 16 s .. 16 s + 15)
     static __device__ __forceinline__ u32x4 frag(const lds_t* tile, int r0, int s, int lane) {
-        return lds_read16(tile, lds_off(r0 + (lane & 31), 2 * s + (lane >> 5)));
+        return lds_read16(tile, k_off(r0 + (lane & 31), 2 * s + (lane >> 5)));
     }
 };
 
 template <int ROWS> struct DtlLoader<ROWS, false> {
     static_assert(ROWS == 256, "MN-contiguous tiles are 256 wide (512-byte k-rows)");
-    static constexpr int NI = 64 * ROWS * 2 / 1024 / (kDtlThreads / 64);  // 4
-    __amdgpu_buffer_rsrc_t rs;
+    static constexpr int NI = kDtlTile / 1024 / (kDtlThreads / 64);
+    u32x4 rs;
     uint32_t voff[NI];
     uint32_t k_bytes;
+    int kr[NI];          // k-row of this lane within the step
     int lds0;
 
     __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
-        rs = make_rsrc(op.ptr, op.bytes);
+        rs = rsrc_words(op.ptr, op.bytes);
         k_bytes = (uint32_t)(op.ld * 2);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int kb = wave * NI + i;              // kilobyte = 2 k-rows
-            const int k = kb * 2 + (lane >> 5);
-            const int c = (lane & 31) ^ ((k & 3) << 1);
+            const int k = (wave * NI + i) * 2 + (lane >> 5);           // 2 k-rows per kilobyte
+            const int c = (lane & 31) ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 4);
+            kr[i] = k;
             voff[i] = (uint32_t)(((int64_t)k * op.ld + m0 + c * 8) * 2);
         }
         lds0 = wave * NI * 1024;
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0, int kend, bool full) {
         const uint32_t koff = (uint32_t)k0 * k_bytes;
-        const int lane = (int)(threadIdx.x & 63);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int k = ((int)(threadIdx.x >> 6) * NI + i) * 2 + (lane >> 5);
-            const bool ok = full || (k0 + k) < kend;
-            dtl_load16(rs, tile + lds0 + i * 1024, ok ? voff[i] + koff : kOOB);
+            const bool ok = full || (k0 + kr[i]) < kend;
+            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] + koff : kOOB);
         }
     }
     // fragment of 32 columns (m) starting at m0, sub-step s: lane l gets
@@ -146,12 +192,26 @@ template <int BM, int BN> struct DtlMma {
     }
 };
 
+// Barrier that orders the waves without a memory fence: the caller has
+// already waited for exactly the loads it needs, and a fence would make the
+// compiler wait for every outstanding load (including the prefetches).
+__device__ __forceinline__ void wave_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS of the engine: one array per pipeline stage.
+struct DtlStages {
+    lds_t* st[kDtlStages];
+};
+
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B, const GemmGeom& g,
-                                              const typename Epi::Params& ep, lds_t* smem) {
+                                              const typename Epi::Params& ep, const DtlStages& lds) {
     static_assert(BM == 256 && BN == 256, "tile shape");
-    constexpr int BK = 64;
-    constexpr int kTileA = BM * 128, kTileB = BN * 128, kStage = kTileA + kTileB;
+    constexpr int BK = kDtlBK;
+    constexpr int kStages = kDtlStages;
     const int total = g.tiles_m * g.tiles_n;
     const int grid = (int)gridDim.x;
     const int per_xcd = grid >> 3;
@@ -167,7 +227,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
     const int tid = (int)threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
 
     DtlLoader<BM, A_KMAJOR> la;
@@ -183,27 +244,33 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
 #pragma unroll
             for (int e = 0; e < 16; ++e) mma.acc[i][j][e] = 0.f;
 
-    if (nk > 0) {
-        const bool full = kbeg + BK <= kend;
-        la.issue(smem, kbeg, kend, full);
-        lb.issue(smem + kTileA, kbeg, kend, full);
-    }
-    const int am = wm * (BM / 2), bn = wn * (BN / 4);
-    for (int it = 0; it < nk; ++it) {
-        lds_t* cur = smem + (it & 1) * kStage;
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of step `it` are in LDS
-        __syncthreads();                      // every wave's are; step it-1's buffer is free
-        if (it + 1 < nk) {
-            lds_t* nxt = smem + ((it + 1) & 1) * kStage;
-            const int k1 = kbeg + (it + 1) * BK;
-            const bool full = k1 + BK <= kend;
-            la.issue(nxt, k1, kend, full);
-            lb.issue(nxt + kTileA, k1, kend, full);
-        }
-        const lds_t* ta = cur;
-        const lds_t* tb = cur + kTileA;
+    auto issue = [&](lds_t* st, int step) {
+        const int k0 = kbeg + step * BK;
+        const bool full = k0 + BK <= kend;
+        la.issue(st, k0, kend, full);
+        lb.issue(st + kDtlTile, k0, kend, full);
+    };
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+    for (int p = 0; p < kStages - 1; ++p)
+        if (p < nk) issue(lds.st[p], p);
+    const int am = wm * (BM / 2), bn = wn * (BN / 4);
+
+    auto step = [&](int it, const lds_t* ta, lds_t* refill) {
+        // this wave's loads of step `it` are in LDS once at most the younger
+        // steps' loads are outstanding
+        // (2 * NI instructions per step and wave)
+        const int younger = min(kStages - 2, nk - 1 - it);
+        constexpr int per = 2 * DtlLoader<BM, A_KMAJOR>::NI;
+        static_assert(DtlLoader<BM, A_KMAJOR>::NI == DtlLoader<BN, B_KMAJOR>::NI, "loads per step");
+        if (younger >= 3)      __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * per));
+        else if (younger == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * per));
+        else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | per);
+        else                   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        wave_barrier();         // every wave's loads of step `it` landed; step it-1's buffer is free
+        if (it + kStages - 1 < nk) issue(refill, it + kStages - 1);
+        const lds_t* tb = ta + kDtlTile;
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
             u32x4 a[Mma::FM], b[Mma::FN];
 #pragma unroll
             for (int i = 0; i < Mma::FM; ++i) a[i] = DtlLoader<BM, A_KMAJOR>::frag(ta, am + 32 * i, s, lane);
@@ -216,9 +283,15 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                     mma.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), mma.acc[i][j], 0, 0, 0);
         }
+    };
+    // unrolled by the stage count so that every step names its stage arrays statically
+    for (int it = 0; it < nk; it += kStages) {
+#pragma unroll
+        for (int u = 0; u < kStages; ++u)
+            if (it + u < nk) step(it + u, lds.st[u], lds.st[(u + kStages - 1) % kStages]);
     }
     __syncthreads();   // LDS is reused by epilogues
-    Epi::apply(mma, m0, n0, split, wm, wn, lane, tid, smem, ep);
+    Epi::apply(mma, m0, n0, split, wm, wn, lane, tid, lds.st[0], ep);
 }
 
 }  // namespace kd
