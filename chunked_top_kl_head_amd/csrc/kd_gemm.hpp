@@ -38,7 +38,7 @@ template <> struct Elem<float>  { static constexpr int size = 4; };
 struct Operand {
     const void* ptr;   // element (m, k) at ptr + (kmajor ? m*ld + k : k*ld + m)
     int64_t ld;        // leading dimension, elements
-    uint32_t bytes;    // readable bytes from ptr (loads beyond return 0)
+    uint64_t bytes;    // readable bytes from ptr (loads beyond return 0)
 };
 
 struct GemmGeom {
@@ -76,7 +76,7 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, true> {
     u32x4 reg[NCH];
 
     __device__ __forceinline__ void init(const Operand& op, int m0, int tid) {
-        rs = make_rsrc(op.ptr, op.bytes);
+        rs = make_rsrc(op.ptr, (uint32_t)op.bytes);
         c = tid & 7;
         r0 = tid >> 3;
 #pragma unroll
@@ -115,7 +115,7 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, false> {
     u32x4 reg[BPT][EPC];
 
     __device__ __forceinline__ void init(const Operand& op, int m0, int tid) {
-        rs = make_rsrc(op.ptr, op.bytes);
+        rs = make_rsrc(op.ptr, (uint32_t)op.bytes);
         k_bytes = (uint32_t)(op.ld * ES);
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {

@@ -32,9 +32,16 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 // Raw buffer descriptor as four dwords (gfx9: 48-bit base, stride 0,
 // num_records = bytes, 32-bit data format).
-__device__ __forceinline__ u32x4 rsrc_words(const void* p, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
+__device__ __forceinline__ u32x4 rsrc_words(uint64_t a, uint32_t bytes) {
     return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// Descriptor of the window [base + off, end of operand): the loaders rebase
+// every K step so that all per-lane offsets stay far below 2^31 whatever the
+// operand size.  Windows that start past the end get no records (all zeros).
+__device__ __forceinline__ u32x4 window_rsrc(const Operand& op, uint64_t off) {
+    const uint64_t rec = op.bytes > off ? op.bytes - off : 0;
+    return rsrc_words(reinterpret_cast<uint64_t>(op.ptr) + off, (uint32_t)(rec < 0x7FFFFFFFull ? rec : 0x7FFFFFFFull));
 }
 
 // One direct-to-LDS load: lane l's 16 bytes at byte offset `voff` of the
@@ -108,28 +115,30 @@ template <int ROWS> struct DtlLoader<ROWS, true> {
     static constexpr int NI = kDtlTile / 1024 / (kDtlThreads / 64);
     static constexpr int RPK = 1024 / kRowBytes;                  // rows per kilobyte
     static constexpr int CPR = kRowBytes / 16;                    // chunks per row
-    u32x4 rs;
-    uint32_t voff[NI];
+    Operand op;
+    uint64_t tile_off;   // byte offset of the tile's first row
+    uint32_t voff[NI];   // lane offsets from (tile row 0, step k0)
     int kl[NI];          // element offset of this lane's chunk within the step
     int lds0;            // LDS byte offset of this wave's first kilobyte
 
-    __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
-        rs = rsrc_words(op.ptr, op.bytes);
+    __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
+        op = o;
+        tile_off = (uint64_t)m0 * (uint64_t)o.ld * 2u;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int r = (wave * NI + i) * RPK + lane / CPR;
             const int c = (lane % CPR) ^ k_swz(r);                   // logical chunk at this lane's slot
             kl[i] = c * 8;
-            voff[i] = (uint32_t)(((int64_t)(m0 + r) * op.ld + c * 8) * 2);
+            voff[i] = (uint32_t)(((int64_t)r * o.ld + c * 8) * 2);
         }
         lds0 = wave * NI * 1024;
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0, int kend, bool full) {
-        const uint32_t koff = (uint32_t)(k0 * 2);
+        const u32x4 rs = window_rsrc(op, tile_off + (uint64_t)k0 * 2u);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const bool ok = full || (k0 + kl[i]) < kend;
-            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] + koff : kOOB);
+            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] : kOOB);
         }
     }
     // fragment of 32 rows starting at row r0, sub-step s (k = 16 s .. 16 s + 15)
@@ -141,30 +150,30 @@ template <int ROWS> struct DtlLoader<ROWS, true> {
 template <int ROWS> struct DtlLoader<ROWS, false> {
     static_assert(ROWS == 256, "MN-contiguous tiles are 256 wide (512-byte k-rows)");
     static constexpr int NI = kDtlTile / 1024 / (kDtlThreads / 64);
-    u32x4 rs;
-    uint32_t voff[NI];
-    uint32_t k_bytes;
+    Operand op;
+    uint64_t tile_off;   // byte offset of the tile's first column
+    uint32_t voff[NI];   // lane offsets from (step k0, tile column 0)
     int kr[NI];          // k-row of this lane within the step
     int lds0;
 
-    __device__ __forceinline__ void init(const Operand& op, int m0, int wave, int lane) {
-        rs = rsrc_words(op.ptr, op.bytes);
-        k_bytes = (uint32_t)(op.ld * 2);
+    __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
+        op = o;
+        tile_off = (uint64_t)m0 * 2u;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int k = (wave * NI + i) * 2 + (lane >> 5);           // 2 k-rows per kilobyte
             const int c = (lane & 31) ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 4);
             kr[i] = k;
-            voff[i] = (uint32_t)(((int64_t)k * op.ld + m0 + c * 8) * 2);
+            voff[i] = (uint32_t)(((int64_t)k * o.ld + c * 8) * 2);
         }
         lds0 = wave * NI * 1024;
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0, int kend, bool full) {
-        const uint32_t koff = (uint32_t)k0 * k_bytes;
+        const u32x4 rs = window_rsrc(op, tile_off + (uint64_t)k0 * (uint64_t)op.ld * 2u);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const bool ok = full || (k0 + kr[i]) < kend;
-            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] + koff : kOOB);
+            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] : kOOB);
         }
     }
     // fragment of 32 columns (m) starting at m0, sub-step s: lane l gets

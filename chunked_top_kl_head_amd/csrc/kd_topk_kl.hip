@@ -112,7 +112,8 @@ static int64_t default_chunk(int64_t d, int64_t V, int es) {
     (void)d;
     const int64_t V_pad = cdiv(V, BM) * BM;
     int64_t C = 4096;
-    while (C > 256 && (C + BN) * V_pad * es >= kOperandLimit) C -= 256;
+    if (es == 4)
+        while (C > 256 && (C + BN) * V_pad * es >= kOperandLimit) C -= 256;
     return C;
 }
 
@@ -150,11 +151,13 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
     q.V_pad = cdiv(q.V, BM) * BM;
     q.nvt = q.V_pad / BM;
     q.C = p->chunk > 0 ? p->chunk : default_chunk(q.d, q.V, q.es);
-    // Operands are addressed with 32-bit buffer offsets; a tile may overhang an
-    // operand's end by up to one tile, and every such offset must stay below 2^31.
-    if ((q.V_pad + BM) * q.d * q.es >= kOperandLimit || (q.C + BN) * q.V_pad * q.es >= kOperandLimit ||
-        (q.C + BN) * q.d * q.es >= kOperandLimit || q.C > (1 << 24))
+    // The fp32 engine addresses operands with 32-bit buffer offsets (a tile may
+    // overhang an operand's end by one tile); the bf16 engine rebases its
+    // descriptors per tile and K step and has no such limit.
+    if (q.es == 4 && ((q.V_pad + BM) * q.d * q.es >= kOperandLimit || (q.C + BN) * q.V_pad * q.es >= kOperandLimit ||
+                      (q.C + BN) * q.d * q.es >= kOperandLimit))
         return KD_ERR_UNSUPPORTED;
+    if (q.C > (1 << 20) || q.d > (1 << 20)) return KD_ERR_UNSUPPORTED;
     const int bk = 128 / q.es;
     q.splits = choose_splits(cdiv(q.d, BM) * cdiv(q.C, BN), q.V_pad, bk);
     size_t o = 0;
@@ -190,7 +193,7 @@ static dim3 gemm_grid(const GemmGeom& g, int splits) {
 
 static inline Operand operand(const void* ptr, int64_t ld, int64_t bytes) {
     Operand o;
-    o.ptr = ptr; o.ld = ld; o.bytes = (uint32_t)bytes;
+    o.ptr = ptr; o.ld = ld; o.bytes = (uint64_t)bytes;
     return o;
 }
 

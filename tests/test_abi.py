@@ -94,8 +94,17 @@ def test_workspace_by_op(lib):
 def test_default_chunk(lib):
     assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=201088, K=100))) == 4096
     assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(K=0))) == 0
-    c = lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=2000000, K=100)))
+    # bf16 operands are addressed through rebased descriptors: no size cap
+    assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=2000000, K=100))) == 4096
+    # fp32 operands keep 32-bit offsets: the chunk shrinks
+    c = lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=64, V=500000, K=100, dtype=B.KD_F32)))
     assert 256 <= c < 4096 and c % 256 == 0
+
+
+def test_large_bf16_chunk_accepted(lib):
+    # chunk x V_pad x 2 bytes well beyond 2^31
+    st, n = ws_size(lib, prob(T=65536, d=2880, V=201088, K=100, chunk=16384), B.KD_OP_FUSED)
+    assert st == B.KD_OK and n >= 16384 * 201216 * 2
 
 
 def call_fwd(lib, p, H=P16, W=P16b, idx=P4, lg=P4, ig=None, loss=P4, lse=P4, rl=None, ws=P16, wsb=1 << 40):
