@@ -45,8 +45,28 @@ struct GemmGeom {
     int M, N, K;          // extents (elements)
     int tiles_m, tiles_n;
     int k_per_split;      // K elements per split (multiple of the K step), grid.y = splits
-    int n_fastest;        // 1: consecutive tiles walk N (share the A tile), 0: walk M
+    int group_m;          // tile order: groups of group_m M-tiles, M fastest inside a group, then N
 };
+
+// Logical tile of workgroup b.  The hardware dispatches workgroup b to XCD
+// b % 8; the remap gives every XCD a contiguous range of logical tiles, and the
+// grouped order makes the ~32 workgroups resident on one XCD cover a
+// group_m x (32 / group_m) block of tiles, so that each K step's operand slices
+// are shared in that XCD's L2.  Returns false for the padding workgroups.
+__device__ __forceinline__ bool tile_of(const GemmGeom& g, int& tm, int& tn) {
+    const int total = g.tiles_m * g.tiles_n;
+    const int per_xcd = (int)gridDim.x >> 3;                 // grid is a multiple of 8
+    const int pid = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+    if (pid >= total) return false;
+    const int gsize = g.group_m * g.tiles_n;
+    const int grp = pid / gsize;
+    const int first_m = grp * g.group_m;
+    const int gm = min(g.tiles_m - first_m, g.group_m);
+    const int local = pid - grp * gsize;
+    tm = first_m + local % gm;
+    tn = local / gm;
+    return true;
+}
 
 __device__ __forceinline__ u32x4 lds_read16(const lds_t* base, int off) {
     return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
@@ -244,17 +264,8 @@ __device__ __forceinline__ void gemm_body(const Operand& A, const Operand& B, co
                                           const typename Epi::Params& ep, lds_t* smem) {
     constexpr int ES = Elem<E>::size;
     constexpr int BK = 128 / ES;
-    // XCD-aware remap: hardware dispatches workgroup b to XCD b % 8; give each
-    // XCD a contiguous range of logical tiles so that tiles sharing an operand
-    // tile run under the same L2.
-    const int total = g.tiles_m * g.tiles_n;
-    const int grid = (int)gridDim.x;            // multiple of 8
-    const int per_xcd = grid >> 3;
-    const int pid = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
-    if (pid >= total) return;
     int tm, tn;
-    if (g.n_fastest) { tm = pid / g.tiles_n; tn = pid % g.tiles_n; }
-    else             { tn = pid / g.tiles_m; tm = pid % g.tiles_m; }
+    if (!tile_of(g, tm, tn)) return;
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = (int)blockIdx.y;
     const int kbeg = split * g.k_per_split;

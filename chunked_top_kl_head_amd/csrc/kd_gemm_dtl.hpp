@@ -104,15 +104,18 @@ __device__ __forceinline__ int mn_off(int k, int m) {
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS loaders of one K step of a 256-row operand.  Every wave issues
-// NI instructions of 1 KiB; instruction i of wave w fills LDS kilobyte
-// w * NI + i of the tile.
+// Direct-to-LDS loaders of one K step of a 256-row operand.  Only the first
+// kLoaderWaves waves (one per SIMD) issue loads: NI instructions of 1 KiB each,
+// instruction i of loader wave w filling LDS kilobyte w * NI + i of the tile.
+// A wave waiting on a full texture-address queue stalls at issue; keeping the
+// other wave of each SIMD free of loads lets it feed the matrix core meanwhile.
 // ---------------------------------------------------------------------------
+constexpr int kLoaderWaves = 4;
 template <int ROWS, bool KMAJOR> struct DtlLoader;
 
 template <int ROWS> struct DtlLoader<ROWS, true> {
     static_assert(ROWS == 256, "tile rows");
-    static constexpr int NI = kDtlTile / 1024 / (kDtlThreads / 64);
+    static constexpr int NI = kDtlTile / 1024 / kLoaderWaves;
     static constexpr int RPK = 1024 / kRowBytes;                  // rows per kilobyte
     static constexpr int CPR = kRowBytes / 16;                    // chunks per row
     Operand op;
@@ -149,7 +152,7 @@ template <int ROWS> struct DtlLoader<ROWS, true> {
 
 template <int ROWS> struct DtlLoader<ROWS, false> {
     static_assert(ROWS == 256, "MN-contiguous tiles are 256 wide (512-byte k-rows)");
-    static constexpr int NI = kDtlTile / 1024 / (kDtlThreads / 64);
+    static constexpr int NI = kDtlTile / 1024 / kLoaderWaves;
     Operand op;
     uint64_t tile_off;   // byte offset of the tile's first column
     uint32_t voff[NI];   // lane offsets from (step k0, tile column 0)
@@ -221,14 +224,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     static_assert(BM == 256 && BN == 256, "tile shape");
     constexpr int BK = kDtlBK;
     constexpr int kStages = kDtlStages;
-    const int total = g.tiles_m * g.tiles_n;
-    const int grid = (int)gridDim.x;
-    const int per_xcd = grid >> 3;
-    const int pid = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
-    if (pid >= total) return;
     int tm, tn;
-    if (g.n_fastest) { tm = pid / g.tiles_n; tn = pid % g.tiles_n; }
-    else             { tn = pid / g.tiles_m; tm = pid % g.tiles_m; }
+    if (!tile_of(g, tm, tn)) return;
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = (int)blockIdx.y;
     const int kbeg = split * g.k_per_split;
@@ -240,10 +237,13 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
 
+    const bool loader = wave < kLoaderWaves;
     DtlLoader<BM, A_KMAJOR> la;
     DtlLoader<BN, B_KMAJOR> lb;
-    la.init(A, m0, wave, lane);
-    lb.init(B, n0, wave, lane);
+    if (loader) {
+        la.init(A, m0, wave, lane);
+        lb.init(B, n0, wave, lane);
+    }
     using Mma = DtlMma<BM, BN>;
     Mma mma;
 #pragma unroll
@@ -254,6 +254,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
             for (int e = 0; e < 16; ++e) mma.acc[i][j][e] = 0.f;
 
     auto issue = [&](lds_t* st, int step) {
+        if (!loader) return;
         const int k0 = kbeg + step * BK;
         const bool full = k0 + BK <= kend;
         la.issue(st, k0, kend, full);
@@ -266,8 +267,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
 
     auto step = [&](int it, const lds_t* ta, lds_t* refill) {
         // this wave's loads of step `it` are in LDS once at most the younger
-        // steps' loads are outstanding
-        // (2 * NI instructions per step and wave)
+        // steps' loads are outstanding (2 * NI instructions per step and
+        // loader wave; the other waves have none)
         const int younger = min(kStages - 2, nk - 1 - it);
         constexpr int per = 2 * DtlLoader<BM, A_KMAJOR>::NI;
         static_assert(DtlLoader<BM, A_KMAJOR>::NI == DtlLoader<BN, B_KMAJOR>::NI, "loads per step");

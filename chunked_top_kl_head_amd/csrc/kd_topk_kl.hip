@@ -21,6 +21,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 
 #include "kd_kernels.hpp"
@@ -176,13 +177,17 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
 
 static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-static GemmGeom geom(int64_t M, int64_t N, int64_t K, int splits, int bk, int n_fastest) {
+#ifndef KD_GROUP_M
+#define KD_GROUP_M 4
+#endif
+
+static GemmGeom geom(int64_t M, int64_t N, int64_t K, int splits, int bk) {
     GemmGeom g;
     g.M = (int)M; g.N = (int)N; g.K = (int)K;
     g.tiles_m = (int)cdiv(M, BM);
     g.tiles_n = (int)cdiv(N, BN);
     g.k_per_split = (int)(cdiv(cdiv(K, splits), bk) * bk);
-    g.n_fastest = n_fastest;
+    g.group_m = (int)std::min<int64_t>(KD_GROUP_M, g.tiles_m);
     return g;
 }
 
@@ -227,7 +232,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             StageScope scope(KD_STAGE_LOGITS, stream);
             const Operand A = operand(W, pl.d, pl.V * pl.d * es);
             const Operand B = operand(Hc, pl.d, rc * pl.d * es);
-            const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk, 1);
+            const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk);
             LogitsParams lp{};
             lp.stats = stats; lp.E = G; lp.V = (int)pl.V; lp.V_pad = (int)pl.V_pad; lp.nvt = (int)pl.nvt;
             lp.rows = (int)rc; lp.scale2 = scale2; lp.hdr = hdr;
@@ -264,7 +269,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
         {
             const Operand A = operand(W, pl.d, pl.V * pl.d * es);
             const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
-            const GemmGeom g = geom(pl.d, rc, pl.V_pad, pl.splits, bk, 1);
+            const GemmGeom g = geom(pl.d, rc, pl.V_pad, pl.splits, bk);
             GradHParams hp{};
             hp.out = static_cast<char*>(grad_H) + t0 * pl.d * es;
             hp.partial = part; hp.d = (int)pl.d; hp.rows = (int)rc; hp.C = (int)pl.C;
@@ -285,7 +290,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             StageScope scope(KD_STAGE_GRAD_W, stream);
             const Operand A = operand(Hc, pl.d, rc * pl.d * es);
             const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
-            const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 0);
+            const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk);
             GradWParams wp{};
             wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0;
             launch_gemm<E, false, false, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp);
