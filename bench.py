@@ -30,7 +30,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "fwd+bwd tokens/s of fused top-K KL loss; MFMA util % of bf16 peak; peak HBM GiB"
-KERNEL_SOURCES = ("kd_common.hpp", "kd_gemm.hpp", "kd_kernels.hpp", "kd_topk_kl.hip")
+KERNEL_SOURCES = ("kd_common.hpp", "kd_gemm.hpp", "kd_gemm_dtl.hpp", "kd_kernels.hpp", "kd_topk_kl.hip")
 
 
 def kernel_source_hash() -> str:
@@ -96,8 +96,11 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=0, help="rows per chunk (0 = the workload's)")
     ap.add_argument("--mode", default="fused", choices=["fused", "split"],
                     help="fused entry, or forward followed by backward")
-    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-bytes", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many bytes (a kernel of known "
+                         "traffic, used to scale the FETCH_SIZE/WRITE_SIZE counters of a profiling run)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -247,6 +250,14 @@ def main() -> int:
         "roofline": roof,
         "input_gen_s": round(gen_s, 1),
     }
+    if args.copy_calibration_bytes > 0:
+        src = torch.ones(args.copy_calibration_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_calibration_bytes
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, min(args.cpu_rows, T))
     print(json.dumps(out), flush=True)

@@ -51,10 +51,15 @@ __device__ __forceinline__ u32x4 window_rsrc(const Operand& op, uint64_t off) {
 // reads.  Completion is awaited explicitly with s_waitcnt vmcnt(N) before the
 // barrier that publishes a stage.
 __device__ __forceinline__ void dtl_load16(const u32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
-                 : "memory", "m0");
+    uint32_t saved;   // m0 is restored, so the compiler's own uses of it are unaffected
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(lds_addr)
+        : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const lds_t* p) {

@@ -109,10 +109,13 @@ struct StageScope {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Default rows per chunk.  Larger chunks cut the grad_W read-modify-write
+// traffic (once per chunk) at O(C V) workspace; 8192 rows of bf16 logits at a
+// 201,088-token vocabulary are 3.3 GB, small next to 288 GB of HBM.
 static int64_t default_chunk(int64_t d, int64_t V, int es) {
     (void)d;
     const int64_t V_pad = cdiv(V, BM) * BM;
-    int64_t C = 4096;
+    int64_t C = 8192;
     if (es == 4)
         while (C > 256 && (C + BN) * V_pad * es >= kOperandLimit) C -= 256;
     return C;

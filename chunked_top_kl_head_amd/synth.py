@@ -70,12 +70,12 @@ WORKLOADS = {
     "llama3b": Workload("llama3b", T=8192, d=3072, V=128256, K=100, tau=1.0,
                         dtype="bf16", chunk=1024, mask=("random", 0.05), seed_index=1),
     "gptoss20b": Workload("gptoss20b", T=32768, d=2880, V=201088, K=100, tau=1.0,
-                          dtype="bf16", chunk=4096, mask=None, seed_index=2),
+                          dtype="bf16", chunk=8192, mask=None, seed_index=2),
     "batched4x32k": Workload("batched4x32k", T=131072, d=2880, V=201088, K=100, tau=2.0,
-                             dtype="bf16", chunk=4096, mask=("trailing", 0.1, 32768),
+                             dtype="bf16", chunk=8192, mask=("trailing", 0.1, 32768),
                              seed_index=3),
     "extreme256k": Workload("extreme256k", T=262144, d=2880, V=201088, K=100, tau=1.0,
-                            dtype="bf16", chunk=4096, mask=None, seed_index=4),
+                            dtype="bf16", chunk=8192, mask=None, seed_index=4),
 }
 
 

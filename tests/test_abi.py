@@ -92,13 +92,13 @@ def test_workspace_by_op(lib):
 
 
 def test_default_chunk(lib):
-    assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=201088, K=100))) == 4096
+    assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=201088, K=100))) == 8192
     assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(K=0))) == 0
     # bf16 operands are addressed through rebased descriptors: no size cap
-    assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=2000000, K=100))) == 4096
+    assert lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=2880, V=2000000, K=100))) == 8192
     # fp32 operands keep 32-bit offsets: the chunk shrinks
     c = lib.kd_topk_kl_default_chunk(ctypes.byref(prob(d=64, V=500000, K=100, dtype=B.KD_F32)))
-    assert 256 <= c < 4096 and c % 256 == 0
+    assert 256 <= c < 8192 and c % 256 == 0
 
 
 def test_large_bf16_chunk_accepted(lib):
