@@ -16,11 +16,11 @@
 //     (512-byte k-rows, 16-byte chunks XOR-swizzled by k); fragments are two
 //     ds_read_b64_tr_b16 per lane, which transpose 4 x 16 blocks across the
 //     16 lanes of a quarter-wave.
-// kDtlStages LDS stages (one K step of kDtlBK each): all but one are in flight
-// while one is consumed; each step waits only for its own loads, meets at one
-// barrier, issues the step kDtlStages - 1 ahead, then runs kDtlBK / 16 MFMA
-// sub-steps.
+// Two LDS stages of one 64-deep K step each: one is consumed while the loads of
+// the other are in flight (see the main loop below).
 #pragma once
+
+#include <type_traits>
 
 #include "kd_gemm.hpp"
 
@@ -50,7 +50,13 @@ __device__ __forceinline__ u32x4 window_rsrc(const Operand& op, uint64_t off) {
 // compiler does not add its own conservative vmcnt waits before unrelated LDS
 // reads.  Completion is awaited explicitly with s_waitcnt vmcnt(N) before the
 // barrier that publishes a stage.
-__device__ __forceinline__ void dtl_load16(const u32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+__device__ __forceinline__ void dtl_load16(const u32x4& rsrc_in, uint32_t lds_addr_in, uint32_t voff) {
+    // the descriptor and the LDS address are wave-uniform; make sure they live
+    // in scalar registers (an "s" operand must not be given a vector register)
+    const uint32_t lds_addr = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr_in);
+    u32x4 rsrc;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) rsrc[w] = (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc_in[w]);
     uint32_t saved;   // m0 is restored, so the compiler's own uses of it are unaffected
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -62,6 +68,11 @@ __device__ __forceinline__ void dtl_load16(const u32x4& rsrc, uint32_t lds_addr,
         : "memory");
 }
 
+// Hides a per-lane value from loop-invariant code motion: the compiler would
+// otherwise precompute every load and fragment address of the main loop and
+// run out of registers.
+template <typename T> __device__ __forceinline__ void opaque(T& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ uint32_t lds_addr_of(const lds_t* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
@@ -72,35 +83,21 @@ __device__ __forceinline__ u32x2 lds_read8_tr(const lds_t* base, int off) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-// K step of the engine (bf16 elements) and pipeline depth.  A stage holds the
-// A and B tiles of one step: 2 * 256 * kDtlBK * 2 bytes.
-#ifndef KD_DTL_BK
-#define KD_DTL_BK 64
-#endif
-#ifndef KD_DTL_STAGES
-#define KD_DTL_STAGES 2
-#endif
-constexpr int kDtlBK = KD_DTL_BK;
-constexpr int kDtlStages = KD_DTL_STAGES;
+// K step of the engine (bf16 elements).  An LDS stage holds the A and B tiles
+// of one step, 2 x 256 x 64 x 2 bytes = 64 KiB; two stages are in use.
+constexpr int kDtlBK = 64;
 constexpr int kDtlTile = 256 * kDtlBK * 2;   // bytes of one operand tile per step
-static_assert(kDtlBK == 32 || kDtlBK == 64, "K step");
-static_assert(kDtlStages >= 2 && kDtlStages * 2 * kDtlTile <= 160 * 1024, "stages fit in LDS");
 
-// K-contiguous tile of one step: [rows][kDtlBK] bf16, rows of kDtlBK / 8
+// K-contiguous tile of one step: [rows][64] bf16, 128-byte rows of eight
 // 16-byte chunks.  Chunk c of row r is stored at c ^ k_swz(r), chosen so that
-// a fragment read (32 consecutive rows, one chunk) touches distinct banks
-// whether the LDS serves 8 lanes of a 16-byte read per cycle from 32 banks or
-// 16 lanes from 64 banks.
+// a fragment read (32 consecutive rows, one chunk) touches distinct banks.
 constexpr int kRowBytes = kDtlBK * 2;
-__device__ __forceinline__ int k_swz(int r) {
-    if constexpr (kDtlBK == 64) return (r ^ (r >> 3)) & 7;
-    else return ((r >> 1) ^ (r >> 3)) & 3;
-}
+__device__ __forceinline__ int k_swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int k_off(int r, int c) {
     return r * kRowBytes + ((c ^ k_swz(r)) << 4);
 }
 
-// MN-contiguous tile of one step: [kDtlBK][256] bf16, 512-byte k-rows of 32
+// MN-contiguous tile of one step: [64][256] bf16, 512-byte k-rows of 32
 // chunks; chunk c of k-row k is stored at c ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 4).
 // A transposing read touches k-rows {k0..k0+3} (and k0+8.. in the other half
 // wave) x four consecutive chunks, which this places in distinct banks.
@@ -109,89 +106,129 @@ __device__ __forceinline__ int mn_off(int k, int m) {
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS loaders of one K step of a 256-row operand.  Only the first
-// kLoaderWaves waves (one per SIMD) issue loads: NI instructions of 1 KiB each,
-// instruction i of loader wave w filling LDS kilobyte w * NI + i of the tile.
-// A wave waiting on a full texture-address queue stalls at issue; keeping the
-// other wave of each SIMD free of loads lets it feed the matrix core meanwhile.
+// Direct-to-LDS loaders of one K step of a 256-row operand.  The first
+// kLoaderWaves waves issue the loads: NI instructions of 1 KiB per operand and
+// step, instruction i of loader wave w filling LDS kilobyte w * NI + i of the
+// tile.  Instructions are issued one at a time between matrix instructions so
+// that a wave waiting for room in the texture-address queue delays at most one
+// MFMA of its own, while the other wave of the SIMD keeps the matrix core busy.
 // ---------------------------------------------------------------------------
-constexpr int kLoaderWaves = 4;
+#ifndef KD_STAGGER
+#define KD_STAGGER 0
+#endif
+#ifndef KD_LOADER_WAVES
+#if KD_STAGGER
+#define KD_LOADER_WAVES 8
+#else
+#define KD_LOADER_WAVES 4
+#endif
+#endif
+constexpr int kLoaderWaves = KD_LOADER_WAVES;
+static_assert(kLoaderWaves == 4 || kLoaderWaves == 8, "loader waves");
+
 template <int ROWS, bool KMAJOR> struct DtlLoader;
 
+// K-contiguous operand.  Load instruction i of loader wave w covers tile rows
+// 8 u .. 8 u + 7 (u = w NI + i); lane l reads logical chunk
+// (l & 7) ^ (l >> 3) ^ (u & 7) of row 8 u + (l >> 3), which lands in the
+// swizzled slot l & 7 of that row.
 template <int ROWS> struct DtlLoader<ROWS, true> {
-    static_assert(ROWS == 256, "tile rows");
+    static_assert(ROWS == 256 && kRowBytes == 128, "tile rows and K step");
     static constexpr int NI = kDtlTile / 1024 / kLoaderWaves;
-    static constexpr int RPK = 1024 / kRowBytes;                  // rows per kilobyte
-    static constexpr int CPR = kRowBytes / 16;                    // chunks per row
     Operand op;
     uint64_t tile_off;   // byte offset of the tile's first row
-    uint32_t voff[NI];   // lane offsets from (tile row 0, step k0)
-    int kl[NI];          // element offset of this lane's chunk within the step
-    int lds0;            // LDS byte offset of this wave's first kilobyte
+    uint32_t lrow;       // byte offset of this lane's row within an instruction's rows
+    int zl;              // lane part of the chunk index
 
     __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
         op = o;
-        tile_off = (uint64_t)m0 * (uint64_t)o.ld * 2u;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = (wave * NI + i) * RPK + lane / CPR;
-            const int c = (lane % CPR) ^ k_swz(r);                   // logical chunk at this lane's slot
-            kl[i] = c * 8;
-            voff[i] = (uint32_t)(((int64_t)r * o.ld + c * 8) * 2);
-        }
-        lds0 = wave * NI * 1024;
+        tile_off = (uint64_t)m0 * (uint64_t)o.ld * 2u + (uint64_t)(wave * NI) * 16u * (uint64_t)o.ld;
+        lrow = (uint32_t)(2 * (lane >> 3) * o.ld);
+        zl = (lane & 7) ^ (lane >> 3) ^ ((wave * NI) & 7);
     }
-    __device__ __forceinline__ void issue(lds_t* tile, int k0, int kend, bool full) {
-        const u32x4 rs = window_rsrc(op, tile_off + (uint64_t)k0 * 2u);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const bool ok = full || (k0 + kl[i]) < kend;
-            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] : kOOB);
-        }
+    __device__ __forceinline__ u32x4 rsrc(int k0) const { return window_rsrc(op, tile_off + (uint64_t)k0 * 2u); }
+    __device__ __forceinline__ void hide() {
+        opaque(lrow);
+        opaque(zl);
     }
-    // fragment of 32 rows starting at row r0, sub-step s (k = 16 s .. 16 s + 15)
-    static __device__ __forceinline__ u32x4 frag(const lds_t* tile, int r0, int s, int lane) {
-        return lds_read16(tile, k_off(r0 + (lane & 31), 2 * s + (lane >> 5)));
+    // instruction i of the step at k0 into the tile at LDS byte address `tile`
+    __device__ __forceinline__ void issue1(const u32x4& rs, uint32_t tile, int i, int k0, int kend, bool full,
+                                           int wave) const {
+        const int c = zl ^ i;
+        uint32_t v = lrow + (uint32_t)(i * 16 * op.ld) + (uint32_t)(c << 4);
+        if (!full && k0 + c * 8 >= kend) v = kOOB;
+        dtl_load16(rs, tile + (uint32_t)((wave * NI + i) * 1024), v);
+    }
+    // Fragment addresses: 32-row fragment f (rows base + 32 f ..) of sub-step s
+    // (k = 16 s ..) is at off[s ^ 2 (f & 1)] + 4096 f for this lane.
+    struct Frag {
+        int off[4];
+    };
+    static __device__ __forceinline__ Frag frag_addr(int base, int lane) {
+        const int x = (lane >> 5) ^ (lane & 7) ^ ((lane >> 3) & 3);
+        const int rowb = (base + (lane & 31)) * kRowBytes;
+        Frag f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) f.off[y] = rowb + ((x ^ (2 * y)) << 4);
+        return f;
+    }
+    static __device__ __forceinline__ u32x4 frag(const lds_t* tile, const Frag& fa, int f, int s) {
+        return lds_read16(tile, fa.off[s ^ (2 * (f & 1))] + 4096 * f);
     }
 };
 
+// MN-contiguous operand.  Load instruction i of loader wave w covers k-rows
+// 2 u and 2 u + 1 (u = w NI + i); lane l reads the 16 bytes of k-row
+// 2 u + (l >> 5) whose chunk lands in slot l & 31 of that row.
 template <int ROWS> struct DtlLoader<ROWS, false> {
     static_assert(ROWS == 256, "MN-contiguous tiles are 256 wide (512-byte k-rows)");
     static constexpr int NI = kDtlTile / 1024 / kLoaderWaves;
     Operand op;
-    uint64_t tile_off;   // byte offset of the tile's first column
-    uint32_t voff[NI];   // lane offsets from (step k0, tile column 0)
-    int kr[NI];          // k-row of this lane within the step
-    int lds0;
+    uint64_t tile_off;   // byte offset of the tile's first column at this wave's first k-row
+    uint32_t lrow;       // byte offset of this lane's k-row within an instruction
+    int zl;              // lane part of the chunk index
+    int kw;              // (w NI) / 4, whose parity enters the chunk swizzle
+    int kl;              // this lane's k-row within an instruction (0 or 1)
 
     __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
         op = o;
-        tile_off = (uint64_t)m0 * 2u;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int k = (wave * NI + i) * 2 + (lane >> 5);           // 2 k-rows per kilobyte
-            const int c = (lane & 31) ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 4);
-            kr[i] = k;
-            voff[i] = (uint32_t)(((int64_t)k * o.ld + c * 8) * 2);
-        }
-        lds0 = wave * NI * 1024;
+        tile_off = (uint64_t)m0 * 2u + (uint64_t)(wave * NI) * 4u * (uint64_t)o.ld;
+        kl = lane >> 5;
+        lrow = (uint32_t)(2 * kl * o.ld);
+        zl = (lane & 31) ^ (kl << 2);
+        kw = (wave * NI) >> 2;
     }
-    __device__ __forceinline__ void issue(lds_t* tile, int k0, int kend, bool full) {
-        const u32x4 rs = window_rsrc(op, tile_off + (uint64_t)k0 * (uint64_t)op.ld * 2u);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const bool ok = full || (k0 + kr[i]) < kend;
-            dtl_load16(rs, lds_addr_of(tile) + (uint32_t)(lds0 + i * 1024), ok ? voff[i] : kOOB);
-        }
+    __device__ __forceinline__ u32x4 rsrc(int k0) const {
+        return window_rsrc(op, tile_off + (uint64_t)k0 * (uint64_t)op.ld * 2u);
     }
-    // fragment of 32 columns (m) starting at m0, sub-step s: lane l gets
-    // m = m0 + (l & 31), k = 16 s + 8 (l >> 5) .. + 7
-    static __device__ __forceinline__ u32x4 frag(const lds_t* tile, int m0, int s, int lane) {
+    __device__ __forceinline__ void hide() {
+        opaque(lrow);
+        opaque(zl);
+        opaque(kl);
+    }
+    __device__ __forceinline__ void issue1(const u32x4& rs, uint32_t tile, int i, int k0, int kend, bool full,
+                                           int wave) const {
+        const int c = zl ^ (8 * (i & 1)) ^ (16 * ((kw + (i >> 2)) & 1));
+        uint32_t v = lrow + (uint32_t)(i * 4 * op.ld) + (uint32_t)(c << 4);
+        if (!full && k0 + (wave * NI + i) * 2 + kl >= kend) v = kOOB;
+        dtl_load16(rs, tile + (uint32_t)((wave * NI + i) * 1024), v);
+    }
+    // Fragment f (columns base + 32 f ..) of sub-step s: lane l gets
+    // m = base + 32 f + (l & 31), k = 16 s + 8 (l >> 5) .. + 7, as two
+    // transposing reads at off[f] + 8192 s and + 2048.
+    struct Frag {
+        int off[4];
+    };
+    static __device__ __forceinline__ Frag frag_addr(int base, int lane) {
         const int g = lane >> 4, i = lane & 15;
-        const int mb = m0 + 16 * (g & 1) + 4 * (i & 3);
-        const int kb = 16 * s + 8 * (g >> 1) + (i >> 2);
-        const u32x2 lo = lds_read8_tr(tile, mn_off(kb, mb));
-        const u32x2 hi = lds_read8_tr(tile, mn_off(kb + 4, mb));
+        Frag fa;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) fa.off[f] = mn_off(8 * (g >> 1) + (i >> 2), base + 32 * f + 16 * (g & 1) + 4 * (i & 3));
+        return fa;
+    }
+    static __device__ __forceinline__ u32x4 frag(const lds_t* tile, const Frag& fa, int f, int s) {
+        const u32x2 lo = lds_read8_tr(tile, fa.off[f] + 8192 * s);
+        const u32x2 hi = lds_read8_tr(tile, fa.off[f] + 8192 * s + 2048);
         return u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 };
@@ -211,24 +248,55 @@ template <int BM, int BN> struct DtlMma {
 
 // Barrier that orders the waves without a memory fence: the caller has
 // already waited for exactly the loads it needs, and a fence would make the
-// compiler wait for every outstanding load (including the prefetches).
+// compiler wait for every outstanding load.
 __device__ __forceinline__ void wave_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// LDS of the engine: one array per pipeline stage.
-struct DtlStages {
-    lds_t* st[kDtlStages];
-};
+// LDS of the engine: two pipeline stages of kDtlStage bytes (A tile, then B tile).
+constexpr int kDtlStage = 2 * kDtlTile;
+constexpr int kDtlLds = 2 * kDtlStage;
+constexpr int kDtlEpiLds = 4096;   // epilogue scratch beyond the stages
 
+// ---------------------------------------------------------------------------
+// Main loop.  Per K step a wave runs four sub-steps of eight MFMAs; the
+// operand fragments of sub-step s + 1 are read from LDS while the MFMAs of
+// sub-step s run (two register sets), and the last sub-step's MFMAs run after
+// the barrier that publishes the next stage, so they cover the latency of the
+// next stage's first fragment reads.  The loads of step it + 1 are issued in
+// the first two MFMA groups after that barrier, into the stage every wave has
+// just finished reading, and are awaited at the end of step it.
+// ---------------------------------------------------------------------------
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B, const GemmGeom& g,
-                                              const typename Epi::Params& ep, const DtlStages& lds) {
+                                              const typename Epi::Params& ep, lds_t* smem) {
     static_assert(BM == 256 && BN == 256, "tile shape");
     constexpr int BK = kDtlBK;
-    constexpr int kStages = kDtlStages;
+    using LA = DtlLoader<BM, A_KMAJOR>;
+    using LB = DtlLoader<BN, B_KMAJOR>;
+    using Mma = DtlMma<BM, BN>;
+    constexpr int FM = Mma::FM, FN = Mma::FN;
+    constexpr int NT = LA::NI + LB::NI;          // load instructions per step and loader wave
+    // S0 of them ride on the MFMA group that follows each barrier (for the
+    // step two ahead, the earliest a stage is free), the other S1 on the next
+    // group (for the step after the current one).  Issuing everything as
+    // early as possible measured best: two loads after each of the eight
+    // MFMAs of that group.  kBurst issues a group's share ahead of its MFMAs.
+#ifdef KD_DMA_S0
+    constexpr int S0 = KD_DMA_S0;
+#else
+    constexpr int S0 = NT;
+#endif
+#ifdef KD_DMA_BURST
+    constexpr bool kBurst = KD_DMA_BURST;
+#else
+    constexpr bool kBurst = false;
+#endif
+    constexpr int S1 = NT - S0;
+    static_assert(S0 >= 0 && S1 >= 0, "load shares");
+
     int tm, tn;
     if (!tile_of(g, tm, tn)) return;
     const int m0 = tm * BM, n0 = tn * BN;
@@ -241,72 +309,180 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
-
     const bool loader = wave < kLoaderWaves;
-    DtlLoader<BM, A_KMAJOR> la;
-    DtlLoader<BN, B_KMAJOR> lb;
+
+    LA la;
+    LB lb;
     if (loader) {
         la.init(A, m0, wave, lane);
         lb.init(B, n0, wave, lane);
     }
-    using Mma = DtlMma<BM, BN>;
     Mma mma;
 #pragma unroll
-    for (int i = 0; i < Mma::FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < Mma::FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mma.acc[i][j][e] = 0.f;
 
-    auto issue = [&](lds_t* st, int step) {
-        if (!loader) return;
-        const int k0 = kbeg + step * BK;
-        const bool full = k0 + BK <= kend;
-        la.issue(st, k0, kend, full);
-        lb.issue(st + kDtlTile, k0, kend, full);
+    typename LA::Frag fa = LA::frag_addr(wm * (BM / 2), lane);
+    typename LB::Frag fb = LB::frag_addr(wn * (BN / 4), lane);
+    struct Frags {
+        u32x4 a[FM], b[FN];
     };
+    // FMV: fragments of this wave's rows that hold output rows below M (the
+    // others are neither read nor multiplied)
+    auto read = [&](Frags& f, const lds_t* tile, int s, auto fmv_c) {
+        constexpr int FMV = decltype(fmv_c)::value;
+        if constexpr (FMV == 0) return;
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p)
-        if (p < nk) issue(lds.st[p], p);
-    const int am = wm * (BM / 2), bn = wn * (BN / 4);
-
-    auto step = [&](int it, const lds_t* ta, lds_t* refill) {
-        // this wave's loads of step `it` are in LDS once at most the younger
-        // steps' loads are outstanding (2 * NI instructions per step and
-        // loader wave; the other waves have none)
-        const int younger = min(kStages - 2, nk - 1 - it);
-        constexpr int per = 2 * DtlLoader<BM, A_KMAJOR>::NI;
-        static_assert(DtlLoader<BM, A_KMAJOR>::NI == DtlLoader<BN, B_KMAJOR>::NI, "loads per step");
-        if (younger >= 3)      __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * per));
-        else if (younger == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * per));
-        else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | per);
-        else                   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        wave_barrier();         // every wave's loads of step `it` landed; step it-1's buffer is free
-        if (it + kStages - 1 < nk) issue(refill, it + kStages - 1);
-        const lds_t* tb = ta + kDtlTile;
+        for (int i = 0; i < FMV; ++i) f.a[i] = LA::frag(tile, fa, i, s);
 #pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            u32x4 a[Mma::FM], b[Mma::FN];
+        for (int j = 0; j < FN; ++j) f.b[j] = LB::frag(tile + kDtlTile, fb, j, s);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mfma1 = [&](const Frags& f, int q) {
+        const int i = q / FN, j = q % FN;
+        mma.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
+                                                               __builtin_bit_cast(bf16x8, f.b[j]), mma.acc[i][j], 0, 0, 0);
+    };
+    // loads of one step, in flight between two barriers
+    struct Pending {
+        u32x4 ra, rb;
+        uint32_t tile;
+        int k0;
+        bool full;
+    };
+    auto pending_for = [&](int step, const lds_t* tile) {
+        Pending p;
+        p.k0 = kbeg + step * BK;
+        p.full = p.k0 + BK <= kend;
+        p.ra = la.rsrc(p.k0);
+        p.rb = lb.rsrc(p.k0);
+        p.tile = lds_addr_of(tile);
+        return p;
+    };
+    auto load1 = [&](const Pending& p, int q) {
+        if (q < LA::NI) la.issue1(p.ra, p.tile, q, p.k0, kend, p.full, wave);
+        else            lb.issue1(p.rb, p.tile + kDtlTile, q - LA::NI, p.k0, kend, p.full, wave);
+    };
+    // one MFMA group carrying load instructions first .. first + CNT - 1
+    auto group = [&](const Frags& f, auto with_loads, const Pending& p, auto first_c, auto cnt_c, auto fmv_c) {
+        constexpr int first = decltype(first_c)::value, CNT = decltype(cnt_c)::value;
+        constexpr int NQ = decltype(fmv_c)::value * FN;
+        if constexpr (decltype(with_loads)::value && CNT > 0) {
+            if constexpr (kBurst || NQ == 0) {
 #pragma unroll
-            for (int i = 0; i < Mma::FM; ++i) a[i] = DtlLoader<BM, A_KMAJOR>::frag(ta, am + 32 * i, s, lane);
+                for (int t = 0; t < CNT; ++t) load1(p, first + t);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < Mma::FN; ++j) b[j] = DtlLoader<BN, B_KMAJOR>::frag(tb, bn + 32 * j, s, lane);
+                for (int q = 0; q < NQ; ++q) mfma1(f, q);
+            } else {
+                // load t follows MFMA (t * NQ) / CNT
 #pragma unroll
-            for (int i = 0; i < Mma::FM; ++i)
+                for (int q = 0; q < NQ; ++q) {
+                    mfma1(f, q);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < Mma::FN; ++j)
-                    mma.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), mma.acc[i][j], 0, 0, 0);
+                    for (int t = 0; t < CNT; ++t)
+                        if ((t * NQ) / CNT == q) load1(p, first + t);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) mfma1(f, q);
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
-    // unrolled by the stage count so that every step names its stage arrays statically
-    for (int it = 0; it < nk; it += kStages) {
+    using Z = std::integral_constant<int, 0>;
+
+    // Main loop of one wave whose loads ride as S0c instructions on the group
+    // after each barrier (for the step two ahead) and S1c on the group after
+    // that (for the next step).
+    auto run = [&](auto S0c, auto S1c, auto FMVc) {
+        constexpr int s0 = decltype(S0c)::value, s1 = decltype(S1c)::value;
+        static_assert(s0 + s1 == 0 || s0 + s1 == NT, "a loader wave issues all its instructions");
+        using C0 = std::integral_constant<int, s0>;
+        using C1 = std::integral_constant<int, s1>;
+        Frags f0, f1;
+        if constexpr (s0 + s1 > 0) {
+            // step 0, and the share of step 1 that would have ridden on step -1
+            const Pending p = pending_for(0, smem);
 #pragma unroll
-        for (int u = 0; u < kStages; ++u)
-            if (it + u < nk) step(it + u, lds.st[u], lds.st[(u + kStages - 1) % kStages]);
+            for (int q = 0; q < NT; ++q) load1(p, q);
+            if (nk > 1) {
+                const Pending p1 = pending_for(1, smem + kDtlStage);
+#pragma unroll
+                for (int q = 0; q < s0; ++q) load1(p1, q);
+                __builtin_amdgcn_s_waitcnt(0x0F70 | s0);   // vmcnt(s0): step 0 landed
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+            }
+        }
+        wave_barrier();
+        read(f0, smem, 0, FMVc);
+        // One K step.  LD1 / LD0: this step carries the loads of step it + 1 /
+        // it + 2 (compile-time, so the MFMA groups stay free of branches).
+        auto body = [&](auto LD1, auto LD0, int it) {
+            la.hide();
+            lb.hide();
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                opaque(fa.off[y]);
+                opaque(fb.off[y]);
+            }
+            lds_t* cur = smem + (it & 1) * kDtlStage;
+            lds_t* nxt = smem + ((it + 1) & 1) * kDtlStage;
+            Pending p1{}, p0{};
+            if constexpr (decltype(LD1)::value && s1 > 0) p1 = pending_for(it + 1, nxt);   // free since the last barrier
+            read(f1, cur, 1, FMVc);
+            group(f0, LD1, p1, C0{}, C1{}, FMVc);
+            read(f0, cur, 2, FMVc);
+            group(f1, std::false_type{}, p1, Z{}, Z{}, FMVc);
+            read(f1, cur, 3, FMVc);
+            group(f0, std::false_type{}, p1, Z{}, Z{}, FMVc);
+            if (it + 1 < nk) {
+                // this wave's loads of step it + 1 and its reads of `cur` are complete
+                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+                wave_barrier();                       // every wave's loads landed; `cur` is free
+                read(f0, nxt, 0, FMVc);
+            }
+            if constexpr (decltype(LD0)::value && s0 > 0) p0 = pending_for(it + 2, cur);
+            group(f1, LD0, p0, Z{}, C0{}, FMVc);           // sub-step 3
+        };
+        const std::true_type yes{};
+        const std::false_type no{};
+        int it = 0;
+        for (; it + 2 < nk; ++it) body(yes, yes, it);
+        if (it + 1 < nk) body(yes, no, it++);
+        body(no, no, it);
+    };
+    if (nk > 0) {
+        // rows of this wave's half below M: all (4 fragments), at most 64 (2)
+        // or none (0) -- the last is the hidden-size tail of d = 2880 at
+        // 256-row tiles, a sixteenth of the two gradient contractions
+        const int rem = g.M - m0 - wm * (BM / 2);
+        const int fmv = rem > 64 ? 4 : (rem > 0 ? 2 : 0);
+        using F4 = std::integral_constant<int, 4>;
+        using F2 = std::integral_constant<int, 2>;
+        auto dispatch = [&](auto S0c, auto S1c) {
+            if (fmv == 4)      run(S0c, S1c, F4{});
+            else if (fmv == 2) run(S0c, S1c, F2{});
+            else               run(S0c, S1c, Z{});
+        };
+#if KD_STAGGER
+        // every wave loads; the two waves of a SIMD take turns (wm = 0 right
+        // after the barrier, wm = 1 one group later)
+        if (wm == 0) dispatch(std::integral_constant<int, NT>{}, Z{});
+        else         dispatch(Z{}, std::integral_constant<int, NT>{});
+#else
+        if (loader) dispatch(std::integral_constant<int, S0>{}, std::integral_constant<int, S1>{});
+        else        dispatch(Z{}, Z{});
+#endif
     }
     __syncthreads();   // LDS is reused by epilogues
-    Epi::apply(mma, m0, n0, split, wm, wn, lane, tid, lds.st[0], ep);
+    Epi::apply(mma, m0, n0, split, wm, wn, lane, tid, smem, ep);
 }
 
 }  // namespace kd

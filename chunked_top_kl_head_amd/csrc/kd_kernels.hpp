@@ -48,8 +48,40 @@ struct LogitsParams {
     const WsHeader* hdr;   // kBwd: s
 };
 
+// bf16 logit tiles leave through LDS so that every global store writes whole
+// 512-byte rows: the MFMA layout gives a lane four consecutive vocabulary ids
+// of one chunk row, i.e. 8-byte pieces scattered over 32 rows per store.
+// Staging layout: [t][256] bf16, 16-byte chunk c of row t at c ^ (t & 31).
+__device__ __forceinline__ int stage_off(int t, int chunk) { return t * 512 + ((chunk ^ (t & 31)) << 4); }
+
+template <class Mma>
+__device__ __forceinline__ void stage_write4(lds_t* st, int wm, int wn, int i, int j, int q, int lane, float x0,
+                                             float x1, float x2, float x3) {
+    const int t = Mma::col(wn, j, lane);
+    const int v = Mma::row(wm, i, q, lane);   // multiple of 4
+    const u32x2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(st + stage_off(t, v >> 3) + ((v & 4) << 1)) = w;
+}
+
+// Writes the staged 256 x 256 tile: rows t < rows of dst (row pitch ld
+// elements, first element at column v0), two rows per wave instruction.
+__device__ __forceinline__ void stage_flush(const lds_t* st, uint16_t* dst, int64_t ld, int n0, int v0, int rows,
+                                            int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c = lane & 31;
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+        const int tl = wave * 32 + 2 * k + (lane >> 5);
+        const u32x4 val = lds_read16(st, stage_off(tl, c));
+        const int t = n0 + tl;
+        if (t < rows) *reinterpret_cast<u32x4*>(dst + (int64_t)t * ld + v0 + c * 8) = val;
+    }
+}
+
 template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
     using Params = LogitsParams;
+    static constexpr bool kStaged = Elem<E>::size == 2;   // bf16 engine: 128 KiB of stage LDS to reuse
+    static constexpr int kRedOff = kStaged ? kDtlLds : 0;  // byte offset of the reduction scratch
 
     static __device__ __forceinline__ void store4(const Params& p, int t, int v0, float x0, float x1,
                                                   float x2, float x3) {
@@ -86,10 +118,10 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int t = n0 + Mma::col(wn, j, lane);
-                if (t >= p.rows) continue;
-                const bool kept = (p.ignore == nullptr) || (p.ignore[t] == 0);
+                const bool live = t < p.rows;
+                const bool kept = live && ((p.ignore == nullptr) || (p.ignore[t] == 0));
                 const float st = kept ? s : 0.f;
-                const float l2 = p.lse[t] * kLog2e;
+                const float l2 = live ? p.lse[t] * kLog2e : 0.f;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -97,14 +129,21 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                         float g[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) g[r] = st * fast_exp2(mma.acc[i][j][4 * q + r] - l2);
-                        store4(p, t, m0 + Mma::row(wm, i, q, lane), g[0], g[1], g[2], g[3]);
+                        if constexpr (kStaged)
+                            stage_write4<Mma>(smem, wm, wn, i, j, q, lane, g[0], g[1], g[2], g[3]);
+                        else if (live)
+                            store4(p, t, m0 + Mma::row(wm, i, q, lane), g[0], g[1], g[2], g[3]);
                     }
+            }
+            if constexpr (kStaged) {
+                __syncthreads();
+                stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.V_pad, n0, m0, p.rows, tid);
             }
             return;
         } else {
             // [4][BN]: column max of wm = 0, 1, then column sum of wm = 0, 1
             __attribute__((address_space(3))) float* red =
-                reinterpret_cast<__attribute__((address_space(3))) float*>(smem);
+                reinterpret_cast<__attribute__((address_space(3))) float*>(smem + kRedOff);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 float mx = -INFINITY;
@@ -141,16 +180,30 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                 }
             }
             if constexpr (MODE == kFused) {
+                if constexpr (kStaged) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int t = n0 + Mma::col(wn, j, lane);
-                    if (t >= p.rows) continue;
+                    for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int i = 0; i < FM; ++i)
+                        for (int i = 0; i < FM; ++i)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            store4(p, t, m0 + Mma::row(wm, i, q, lane), mma.acc[i][j][4 * q],
-                                   mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]);
+                            for (int q = 0; q < 4; ++q)
+                                stage_write4<Mma>(smem, wm, wn, i, j, q, lane, mma.acc[i][j][4 * q],
+                                                  mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
+                                                  mma.acc[i][j][4 * q + 3]);
+                    __syncthreads();
+                    stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.V_pad, n0, m0, p.rows, tid);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int t = n0 + Mma::col(wn, j, lane);
+                        if (t >= p.rows) continue;
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                store4(p, t, m0 + Mma::row(wm, i, q, lane), mma.acc[i][j][4 * q],
+                                       mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]);
+                    }
                 }
             }
         }
@@ -213,26 +266,71 @@ struct GradWParams {
 
 template <typename E, int BM, int BN> struct GradWEpi {
     using Params = GradWParams;
+    static constexpr bool kStaged = Elem<E>::size == 2;   // bf16 engine: stage LDS free for the epilogue
+
     template <class Mma>
-    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int,
-                                                 lds_t*, const Params& p) {
+    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int tid,
+                                                 lds_t* smem, const Params& p) {
         constexpr int FM = Mma::FM, FN = Mma::FN;
+        if constexpr (kStaged) {
+            // Two passes over halves of 128 hidden indices (owned by the waves
+            // with wm = half): the half tile goes to LDS as [v][128] fp32
+            // (16-byte chunk c of row v at c ^ (v & 31)), then every wave
+            // updates whole 512-byte row segments of grad_W.
+            const int wave = tid >> 6;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int v = n0 + Mma::col(wn, j, lane);
-            if (v >= p.V) continue;
+            for (int half = 0; half < 2; ++half) {
+                if (wm == half) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                    for (int j = 0; j < FN; ++j) {
+                        const int v = Mma::col(wn, j, lane);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int h = m0 + Mma::row(wm, i, q, lane);
-                    if (h >= p.d) continue;
-                    f32x4* dst = reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h);
-                    f32x4 val = {mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
-                                 mma.acc[i][j][4 * q + 3]};
-                    if (p.accumulate) val += *dst;
-                    *dst = val;
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int h = Mma::row(0, i, q, lane);   // within the half, multiple of 4
+                                const f32x4 val = {mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1],
+                                                   mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]};
+                                *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(
+                                    smem + v * 512 + (((h >> 2) ^ (v & 31)) << 4)) = val;
+                            }
+                    }
                 }
+                __syncthreads();
+                const int c = lane & 31;
+                const int h = m0 + 128 * half + 4 * c;
+#pragma unroll 8
+                for (int k = 0; k < 16; ++k) {
+                    const int vl = wave * 32 + 2 * k + (lane >> 5);
+                    f32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                        smem + vl * 512 + ((c ^ (vl & 31)) << 4));
+                    const int v = n0 + vl;
+                    if (v < p.V && h < p.d) {
+                        f32x4* dst = reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h);
+                        if (p.accumulate) val += *dst;
+                        *dst = val;
+                    }
+                }
+                if (half == 0) __syncthreads();
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int v = n0 + Mma::col(wn, j, lane);
+                if (v >= p.V) continue;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int h = m0 + Mma::row(wm, i, q, lane);
+                        if (h >= p.d) continue;
+                        f32x4* dst = reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h);
+                        f32x4 val = {mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
+                                     mma.acc[i][j][4 * q + 3]};
+                        if (p.accumulate) val += *dst;
+                        *dst = val;
+                    }
+            }
         }
     }
 };

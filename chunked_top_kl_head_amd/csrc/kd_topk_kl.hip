@@ -43,24 +43,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Operand A, Operand B, Ge
 template <bool AK, bool BK, class Epi>
 __global__ __launch_bounds__(kDtlThreads) void gemm_kernel_dtl(Operand A, Operand B, GemmGeom g,
                                                                typename Epi::Params ep) {
-    __shared__ __attribute__((aligned(1024))) char s0[2 * kDtlTile];
-    __shared__ __attribute__((aligned(1024))) char s1[2 * kDtlTile];
-#if KD_DTL_STAGES >= 3
-    __shared__ __attribute__((aligned(1024))) char s2[2 * kDtlTile];
-#endif
-#if KD_DTL_STAGES == 2
-    const DtlStages lds = {{(lds_t*)s0, (lds_t*)s1}};
-#elif KD_DTL_STAGES == 3
-    const DtlStages lds = {{(lds_t*)s0, (lds_t*)s1, (lds_t*)s2}};
-#elif KD_DTL_STAGES == 4
-    __shared__ __attribute__((aligned(1024))) char s3[2 * kDtlTile];
-    const DtlStages lds = {{(lds_t*)s0, (lds_t*)s1, (lds_t*)s2, (lds_t*)s3}};
-#else
-    __shared__ __attribute__((aligned(1024))) char s3[2 * kDtlTile];
-    __shared__ __attribute__((aligned(1024))) char s4[2 * kDtlTile];
-    const DtlStages lds = {{(lds_t*)s0, (lds_t*)s1, (lds_t*)s2, (lds_t*)s3, (lds_t*)s4}};
-#endif
-    gemm_body_dtl<BM, BN, AK, BK, Epi>(A, B, g, ep, lds);
+    __shared__ __attribute__((aligned(1024))) char smem[kDtlLds + kDtlEpiLds];
+    gemm_body_dtl<BM, BN, AK, BK, Epi>(A, B, g, ep, (lds_t*)smem);
 }
 
 // Launch of one contraction on the engine that matches the element type.
