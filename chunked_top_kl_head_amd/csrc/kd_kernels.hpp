@@ -440,6 +440,30 @@ __device__ __forceinline__ float dot_row(const E* h, const E* w, int d, int lane
     return wave_sum(acc);
 }
 
+// bf16 dot product of two rows of d = 8 nc elements with every load of a row
+// issued before the first multiply (NR >= ceil(nc / 64) chunks per lane).
+template <int NR>
+__device__ __forceinline__ float dot_row_bf16_unrolled(const void* h, const void* w, int nc, int lane) {
+    const u32x4* hv = reinterpret_cast<const u32x4*>(h);
+    const u32x4* wv = reinterpret_cast<const u32x4*>(w);
+    u32x4 a[NR], b[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int c = lane + kWave * r;
+        a[r] = c < nc ? hv[c] : u32x4{0u, 0u, 0u, 0u};
+        b[r] = c < nc ? wv[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc = fmaf(bf16_bits_to_f32(a[r][q] & 0xFFFFu), bf16_bits_to_f32(b[r][q] & 0xFFFFu), acc);
+            acc = fmaf(bf16_bits_to_f32(a[r][q] >> 16), bf16_bits_to_f32(b[r][q] >> 16), acc);
+        }
+    return wave_sum(acc);
+}
+
 template <typename E>
 __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     extern __shared__ float dyn[];           // nvt floats (kFused rescale factors)
@@ -509,9 +533,18 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     // 3. student logits at the cached ids
     const int wave = tid >> 6, lane = tid & 63;
     const E* hrow = reinterpret_cast<const E*>(p.H) + (int64_t)t * p.d;
+    const int nc8 = p.d / 8;   // 16-byte chunks of a bf16 row
     for (int k = wave; k < K; k += kThreads / kWave) {
         const E* wrow = reinterpret_cast<const E*>(p.W) + (int64_t)sh_id[k] * p.d;
-        const float z = dot_row<E>(hrow, wrow, p.d, lane);
+        float z;
+        if constexpr (Elem<E>::size == 2) {
+            if (nc8 <= 2 * kWave)      z = dot_row_bf16_unrolled<2>(hrow, wrow, nc8, lane);
+            else if (nc8 <= 4 * kWave) z = dot_row_bf16_unrolled<4>(hrow, wrow, nc8, lane);
+            else if (nc8 <= 6 * kWave) z = dot_row_bf16_unrolled<6>(hrow, wrow, nc8, lane);
+            else                       z = dot_row<E>(hrow, wrow, p.d, lane);
+        } else {
+            z = dot_row<E>(hrow, wrow, p.d, lane);
+        }
         if (lane == 0) sh_a[k] = z * p.inv_tau;
     }
     __syncthreads();
@@ -537,14 +570,30 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
         for (int i = tid; i < p.nvt; i += kThreads) dyn[i] = s * fast_exp2(st[i][0] - lse2);
         __syncthreads();
         if constexpr (Elem<E>::size == 2) {
+            // U chunks per thread in flight: the row is a pure stream
             u32x4* g = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.G) + grow);
             const int nch = p.V_pad / 8;
-            for (int c = tid; c < nch; c += kThreads) {
-                const float f = dyn[(c * 8) / 256];
-                u32x4 v = g[c];
+            constexpr int U = 8;
+            auto scale = [&](u32x4& v, int c) {
+                const float f = dyn[c >> 5];   // 32 chunks per 256-id tile
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     v[q] = pack_bf16x2(bf16_bits_to_f32(v[q] & 0xFFFFu) * f, bf16_bits_to_f32(v[q] >> 16) * f);
+            };
+            int c = tid;
+            for (; c + (U - 1) * kThreads < nch; c += U * kThreads) {
+                u32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = g[c + u * kThreads];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    scale(v[u], c + u * kThreads);
+                    g[c + u * kThreads] = v[u];
+                }
+            }
+            for (; c < nch; c += kThreads) {
+                u32x4 v = g[c];
+                scale(v, c);
                 g[c] = v;
             }
         } else {
