@@ -258,7 +258,6 @@ __device__ __forceinline__ void wave_barrier() {
 // LDS of the engine: two pipeline stages of kDtlStage bytes (A tile, then B tile).
 constexpr int kDtlStage = 2 * kDtlTile;
 constexpr int kDtlLds = 2 * kDtlStage;
-constexpr int kDtlEpiLds = 4096;   // epilogue scratch beyond the stages
 
 // ---------------------------------------------------------------------------
 // Main loop.  Per K step a wave runs four sub-steps of eight MFMAs; the

@@ -30,18 +30,20 @@ static_assert(sizeof(WsHeader) <= 256, "header slot");
 
 // ---------------------------------------------------------------------------
 // Logit-tile epilogue: the tile is Z^T (rows = vocabulary ids v, columns =
-// chunk rows t).  Per column it reduces the tile's 256 ids to a partial
-// (max, sum of exp) in base 2 -- the online logsumexp of [TH] "Fused chunked
-// KL" is this tiled max/sum plus a merge in the row kernel.
+// chunk rows t).  Each wave reduces its own 128 ids of a column to a partial
+// (max, sum of exp) in base 2, so a 256-id tile leaves two partials per row
+// and no wave waits for another -- the online logsumexp of [TH] "Fused
+// chunked KL" is this blocked max/sum plus a merge in the row kernel.
 //   kStats: write the partials only (forward).
-//   kFused: also write e = exp2(y - tile max) as the MFMA operand of the
+//   kFused: also write e = exp2(y - block max) as the MFMA operand of the
 //           gradient GEMMs (rescaled to G in place by the row kernel).
 //   kBwd  : lse is known: write the dense part of G, s * exp(a - lse), directly.
+constexpr int kStatIds = 128;   // vocabulary ids per (max, sum) partial
 // ---------------------------------------------------------------------------
 struct LogitsParams {
-    f32x2* stats;          // [C][nvt] (max2, sum) per (row, vocab tile)
+    f32x2* stats;          // [C][nst] (max2, sum) per (row, 128-id block)
     void* E;               // [C][V_pad] element type of the operands
-    int V, V_pad, nvt, rows;
+    int V, V_pad, nst, rows;
     float scale2;          // log2(e) / tau
     const float* lse;      // kBwd: natural-log lse of the chunk rows
     const uint8_t* ignore; // kBwd: ignore flags of the chunk rows (may be null)
@@ -81,7 +83,7 @@ __device__ __forceinline__ void stage_flush(const lds_t* st, uint16_t* dst, int6
 template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
     using Params = LogitsParams;
     static constexpr bool kStaged = Elem<E>::size == 2;   // bf16 engine: 128 KiB of stage LDS to reuse
-    static constexpr int kRedOff = kStaged ? kDtlLds : 0;  // byte offset of the reduction scratch
+    static_assert(BM == 2 * kStatIds, "one partial per wave half of the tile");
 
     static __device__ __forceinline__ void store4(const Params& p, int t, int v0, float x0, float x1,
                                                   float x2, float x3) {
@@ -141,9 +143,8 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
             }
             return;
         } else {
-            // [4][BN]: column max of wm = 0, 1, then column sum of wm = 0, 1
-            __attribute__((address_space(3))) float* red =
-                reinterpret_cast<__attribute__((address_space(3))) float*>(smem + kRedOff);
+            // this wave's 128 ids of each of its columns (lanes l and l + 32
+            // hold the same column): max, then exp2 relative to it and the sum
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 float mx = -INFINITY;
@@ -152,32 +153,20 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, mma.acc[i][j][e]);
                 mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-                if (lane < 32) red[wm * BN + Mma::col(wn, j, lane)] = mx;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = Mma::col(wn, j, lane);
-                const float M = fmaxf(red[n], red[BN + n]);
-                float s = 0.f;
+                const bool none = mx == -INFINITY;   // every id of the block is beyond V
+                float sum = 0.f;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const float x = fast_exp2(mma.acc[i][j][e] - M);
+                        const float x = none ? 0.f : fast_exp2(mma.acc[i][j][e] - mx);
                         mma.acc[i][j][e] = x;
-                        s += x;
+                        sum += x;
                     }
-                s += __shfl_xor(s, 32, kWave);
-                if (lane < 32) red[(2 + wm) * BN + n] = s;
-            }
-            __syncthreads();
-            if (tid < BN) {
-                const int t = n0 + tid;
-                if (t < p.rows) {
-                    const f32x2 st = {fmaxf(red[tid], red[BN + tid]), red[2 * BN + tid] + red[3 * BN + tid]};
-                    p.stats[(int64_t)t * p.nvt + m0 / BM] = st;
-                }
+                sum += __shfl_xor(sum, 32, kWave);
+                const int t = n0 + Mma::col(wn, j, lane);
+                if (lane < 32 && t < p.rows)
+                    p.stats[(int64_t)t * p.nst + (m0 / BM) * 2 + wm] = f32x2{mx, sum};
             }
             if constexpr (MODE == kFused) {
                 if constexpr (kStaged) {
@@ -394,14 +383,14 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(WsHeader* hdr, const 
 struct RowParams {
     int mode;
     int t0, rows;
-    int d, V, V_pad, K, nvt;
+    int d, V, V_pad, K, nst;
     float inv_tau;
     const void* H;          // [T][d]
     const void* W;          // [V][d]
     const int32_t* idx;     // [T][K]
     const float* logit;     // [T][K]
     const uint8_t* ignore;  // [T] or null
-    const f32x2* stats;     // [C][nvt]
+    const f32x2* stats;     // [C][nst]
     const float* lse_in;    // [T] (kBwd)
     float* lse_out;         // [T] or null
     float* row_loss;        // [T] or null
@@ -466,7 +455,7 @@ __device__ __forceinline__ float dot_row_bf16_unrolled(const void* h, const void
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
-    extern __shared__ float dyn[];           // nvt floats (kFused rescale factors)
+    extern __shared__ float dyn[];           // nst floats (kFused rescale factors)
     __shared__ float sh_p[kMaxK], sh_lp[kMaxK], sh_a[kMaxK];
     __shared__ int sh_id[kMaxK];
     __shared__ float red[4];
@@ -478,9 +467,9 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     // 1. lse of the row
     float lse2;
     if (p.mode != kBwd) {
-        const f32x2* st = p.stats + (int64_t)r * p.nvt;
+        const f32x2* st = p.stats + (int64_t)r * p.nst;
         float M = -INFINITY, S = 0.f;
-        for (int i = tid; i < p.nvt; i += kThreads) {
+        for (int i = tid; i < p.nst; i += kThreads) {
             const f32x2 v = st[i];
             const float Mn = fmaxf(M, v[0]);
             if (Mn > -INFINITY) S = S * fast_exp2(M - Mn) + v[1] * fast_exp2(v[0] - Mn);
@@ -566,8 +555,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     const float s = p.hdr->s;
     // 5. kFused: e * 2^(tile max - lse2) * s  ->  dense part of G
     if (p.mode == kFused) {
-        const f32x2* st = p.stats + (int64_t)r * p.nvt;
-        for (int i = tid; i < p.nvt; i += kThreads) dyn[i] = s * fast_exp2(st[i][0] - lse2);
+        const f32x2* st = p.stats + (int64_t)r * p.nst;
+        for (int i = tid; i < p.nst; i += kThreads) dyn[i] = s * fast_exp2(st[i][0] - lse2);
         __syncthreads();
         if constexpr (Elem<E>::size == 2) {
             // U chunks per thread in flight: the row is a pure stream
@@ -575,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
             const int nch = p.V_pad / 8;
             constexpr int U = 8;
             auto scale = [&](u32x4& v, int c) {
-                const float f = dyn[c >> 5];   // 32 chunks per 256-id tile
+                const float f = dyn[c >> 4];   // 16 chunks per 128-id block
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     v[q] = pack_bf16x2(bf16_bits_to_f32(v[q] & 0xFFFFu) * f, bf16_bits_to_f32(v[q] >> 16) * f);
@@ -600,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
             f32x4* g = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.G) + grow);
             const int nch = p.V_pad / 4;
             for (int c = tid; c < nch; c += kThreads) {
-                const float f = dyn[(c * 4) / 256];
+                const float f = dyn[(c * 4) / kStatIds];
                 g[c] = g[c] * f;
             }
         }

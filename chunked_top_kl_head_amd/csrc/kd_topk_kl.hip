@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Operand A, Operand B, Ge
 template <bool AK, bool BK, class Epi>
 __global__ __launch_bounds__(kDtlThreads) void gemm_kernel_dtl(Operand A, Operand B, GemmGeom g,
                                                                typename Epi::Params ep) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDtlLds + kDtlEpiLds];
+    __shared__ __attribute__((aligned(1024))) char smem[kDtlLds];
     gemm_body_dtl<BM, BN, AK, BK, Epi>(A, B, g, ep, (lds_t*)smem);
 }
 
@@ -60,7 +60,7 @@ static void launch_gemm(dim3 grid, hipStream_t stream, const Operand& A, const O
 struct Plan {
     int64_t T, d, V, K, C;
     int es;               // element size of H, W, G
-    int64_t V_pad, nvt;
+    int64_t V_pad, nst;   // padded vocabulary; (max, sum) partials per row
     float tau;
     int splits;           // grad_H splits over the vocabulary
     size_t off_hdr, off_closs, off_stats, off_G, off_part, total;
@@ -137,7 +137,7 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
     q.es = p->dtype == KD_BF16 ? 2 : 4;
     q.tau = p->temperature;
     q.V_pad = cdiv(q.V, BM) * BM;
-    q.nvt = q.V_pad / BM;
+    q.nst = q.V_pad / kStatIds;
     q.C = p->chunk > 0 ? p->chunk : default_chunk(q.d, q.V, q.es);
     // The fp32 engine addresses operands with 32-bit buffer offsets (a tile may
     // overhang an operand's end by one tile); the bf16 engine rebases its
@@ -152,7 +152,7 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
     q.off_hdr = o;   o += 256;
     q.off_closs = o; o = align256(o + sizeof(float) * (size_t)q.C);
     q.off_stats = o;
-    if (op != KD_OP_BACKWARD) o = align256(o + sizeof(f32x2) * (size_t)(q.C * q.nvt));
+    if (op != KD_OP_BACKWARD) o = align256(o + sizeof(f32x2) * (size_t)(q.C * q.nst));
     q.off_G = o;
     if (op != KD_OP_FORWARD) o = align256(o + (size_t)(q.C * q.V_pad * q.es));
     q.off_part = o;
@@ -164,17 +164,16 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
 
 static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-#ifndef KD_GROUP_M
-#define KD_GROUP_M 4
-#endif
-
-static GemmGeom geom(int64_t M, int64_t N, int64_t K, int splits, int bk) {
+// Tiles walked M-first in groups of `group` M-tiles, so that the 32 tiles an
+// XCD runs at once share A and B slices in its L2 (measured best: 4 for the
+// logits and grad_H contractions, 8 for grad_W).
+static GemmGeom geom(int64_t M, int64_t N, int64_t K, int splits, int bk, int group = 4) {
     GemmGeom g;
     g.M = (int)M; g.N = (int)N; g.K = (int)K;
     g.tiles_m = (int)cdiv(M, BM);
     g.tiles_n = (int)cdiv(N, BN);
     g.k_per_split = (int)(cdiv(cdiv(K, splits), bk) * bk);
-    g.group_m = (int)std::min<int64_t>(KD_GROUP_M, g.tiles_m);
+    g.group_m = (int)std::min<int64_t>(group, g.tiles_m);
     return g;
 }
 
@@ -221,7 +220,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             const Operand B = operand(Hc, pl.d, rc * pl.d * es);
             const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk);
             LogitsParams lp{};
-            lp.stats = stats; lp.E = G; lp.V = (int)pl.V; lp.V_pad = (int)pl.V_pad; lp.nvt = (int)pl.nvt;
+            lp.stats = stats; lp.E = G; lp.V = (int)pl.V; lp.V_pad = (int)pl.V_pad; lp.nst = (int)pl.nst;
             lp.rows = (int)rc; lp.scale2 = scale2; lp.hdr = hdr;
             lp.lse = lse_in ? lse_in + t0 : nullptr;
             lp.ignore = ignore ? ignore + t0 : nullptr;
@@ -238,14 +237,14 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             RowParams rp{};
             rp.mode = op == KD_OP_FORWARD ? kStats : (op == KD_OP_FUSED ? kFused : kBwd);
             rp.t0 = (int)t0; rp.rows = (int)rc;
-            rp.d = (int)pl.d; rp.V = (int)pl.V; rp.V_pad = (int)pl.V_pad; rp.K = (int)pl.K; rp.nvt = (int)pl.nvt;
+            rp.d = (int)pl.d; rp.V = (int)pl.V; rp.V_pad = (int)pl.V_pad; rp.K = (int)pl.K; rp.nst = (int)pl.nst;
             rp.inv_tau = 1.0f / pl.tau;
             rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.ignore = ignore;
             rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss;
             rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
             {
                 StageScope scope(KD_STAGE_ROWS, stream);
-                hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), (size_t)(pl.nvt * sizeof(float)),
+                hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), (size_t)(pl.nst * sizeof(float)),
                                    stream, rp);
             }
             if (want_loss)
@@ -277,7 +276,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             StageScope scope(KD_STAGE_GRAD_W, stream);
             const Operand A = operand(Hc, pl.d, rc * pl.d * es);
             const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
-            const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk);
+            const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 8);
             GradWParams wp{};
             wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0;
             launch_gemm<E, false, false, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp);
