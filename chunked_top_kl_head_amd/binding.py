@@ -20,6 +20,7 @@ KD_OK, KD_ERR_NULL, KD_ERR_SHAPE, KD_ERR_VALUE, KD_ERR_ALIGN = 0, 1, 2, 3, 4
 KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_HIP, KD_ERR_INTERNAL = 5, 6, 7, 8
 KD_BF16, KD_F32 = 0, 1
 KD_OP_FORWARD, KD_OP_BACKWARD, KD_OP_FUSED = 0, 1, 2
+KD_FLAG_ACCUMULATE_GRAD_W, KD_FLAG_LOGIT_BF16 = 1, 2
 
 # every entry point the header declares
 EXPORTS = (
@@ -29,6 +30,7 @@ EXPORTS = (
     "kd_topk_kl_backward",
     "kd_topk_kl_fused",
     "kd_topk_kl_validate",
+    "kd_topk_kl_scale_grads",
     "kd_topk_kl_set_stage_events",
     "kd_status_string",
 )
@@ -38,7 +40,8 @@ STAGE_NAMES = ("logits", "rows", "grad_H", "grad_W")
 
 class KdProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float)]
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class KdError(RuntimeError):
@@ -73,6 +76,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kd_topk_kl_fused.restype = ctypes.c_int
     lib.kd_topk_kl_validate.argtypes = [prob, vp, vp, vp, vp, vp]
     lib.kd_topk_kl_validate.restype = ctypes.c_int
+    lib.kd_topk_kl_scale_grads.argtypes = [prob, vp, vp, vp, vp]
+    lib.kd_topk_kl_scale_grads.restype = ctypes.c_int
     lib.kd_topk_kl_set_stage_events.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.kd_topk_kl_set_stage_events.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
@@ -92,14 +97,14 @@ def _check(fn: str, status: int):
 
 
 def problem(T: int, d: int, V: int, K: int, temperature: float = 1.0, dtype=torch.bfloat16,
-            chunk: int = 0) -> KdProblem:
+            chunk: int = 0, flags: int = 0) -> KdProblem:
     if dtype == torch.bfloat16:
         dt = KD_BF16
     elif dtype == torch.float32:
         dt = KD_F32
     else:
         raise ValueError(f"unsupported dtype {dtype}")
-    return KdProblem(int(T), int(d), int(V), int(K), int(chunk), dt, float(temperature))
+    return KdProblem(int(T), int(d), int(V), int(K), int(chunk), dt, float(temperature), int(flags), 0)
 
 
 def default_chunk(prob: KdProblem) -> int:
@@ -126,8 +131,8 @@ def _prep(H, W, topk_idx, topk_logit, ignore):
     for name, t in (("H", H), ("W", W), ("topk_idx", topk_idx), ("topk_logit", topk_logit)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
-    if topk_idx.dtype != torch.int32 or topk_logit.dtype != torch.float32:
-        raise ValueError("topk_idx must be int32 and topk_logit float32")
+    if topk_idx.dtype != torch.int32 or topk_logit.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("topk_idx must be int32 and topk_logit float32 or bfloat16")
     if H.dtype != W.dtype:
         raise ValueError("H and W must share a dtype")
     if ignore is not None and (ignore.dtype != torch.uint8 or not ignore.is_cuda or not ignore.is_contiguous()):
@@ -136,6 +141,11 @@ def _prep(H, W, topk_idx, topk_logit, ignore):
     V = W.shape[0]
     K = topk_idx.shape[1] if topk_idx.dim() == 2 else 1
     return T, d, V, K
+
+
+def _flags(topk_logit, accumulate=False) -> int:
+    return (KD_FLAG_LOGIT_BF16 if topk_logit.dtype == torch.bfloat16 else 0) | \
+        (KD_FLAG_ACCUMULATE_GRAD_W if accumulate else 0)
 
 
 def _workspace(prob, op, workspace, device):
@@ -149,7 +159,7 @@ def kd_topk_kl_forward(H, W, topk_idx, topk_logit, ignore=None, temperature=1.0,
                        want_row_loss=False, workspace=None, stream=None):
     """Returns (loss[1], lse[T], row_loss[T] or None)."""
     T, d, V, K = _prep(H, W, topk_idx, topk_logit, ignore)
-    prob = problem(T, d, V, K, temperature, H.dtype, chunk)
+    prob = problem(T, d, V, K, temperature, H.dtype, chunk, _flags(topk_logit))
     ws, _ = _workspace(prob, KD_OP_FORWARD, workspace, H.device)
     loss = torch.empty(1, dtype=torch.float32, device=H.device)
     lse = torch.empty(T, dtype=torch.float32, device=H.device)
@@ -162,10 +172,12 @@ def kd_topk_kl_forward(H, W, topk_idx, topk_logit, ignore=None, temperature=1.0,
 
 
 def kd_topk_kl_backward(H, W, topk_idx, topk_logit, lse, ignore=None, grad_loss=None, temperature=1.0, chunk=0,
-                        workspace=None, stream=None, grad_H=None, grad_W=None):
-    """Returns (grad_H[T, d] in H's dtype, grad_W[V, d] fp32)."""
+                        workspace=None, stream=None, grad_H=None, grad_W=None, accumulate=False):
+    """Returns (grad_H[T, d] in H's dtype, grad_W[V, d] fp32).  accumulate: add into the given grad_W."""
     T, d, V, K = _prep(H, W, topk_idx, topk_logit, ignore)
-    prob = problem(T, d, V, K, temperature, H.dtype, chunk)
+    if accumulate and grad_W is None:
+        raise ValueError("accumulate needs the grad_W to add into")
+    prob = problem(T, d, V, K, temperature, H.dtype, chunk, _flags(topk_logit, accumulate))
     ws, _ = _workspace(prob, KD_OP_BACKWARD, workspace, H.device)
     gH = torch.empty_like(H) if grad_H is None else grad_H
     gW = torch.empty((V, d), dtype=torch.float32, device=H.device) if grad_W is None else grad_W
@@ -178,10 +190,12 @@ def kd_topk_kl_backward(H, W, topk_idx, topk_logit, lse, ignore=None, grad_loss=
 
 def kd_topk_kl_fused(H, W, topk_idx, topk_logit, ignore=None, grad_loss=None, temperature=1.0, chunk=0,
                      want_lse=False, want_row_loss=False, workspace=None, stream=None, grad_H=None, grad_W=None,
-                     loss=None):
-    """Returns (loss[1], grad_H, grad_W, lse or None, row_loss or None)."""
+                     loss=None, accumulate=False):
+    """Returns (loss[1], grad_H, grad_W, lse or None, row_loss or None).  accumulate: add into the given grad_W."""
     T, d, V, K = _prep(H, W, topk_idx, topk_logit, ignore)
-    prob = problem(T, d, V, K, temperature, H.dtype, chunk)
+    if accumulate and grad_W is None:
+        raise ValueError("accumulate needs the grad_W to add into")
+    prob = problem(T, d, V, K, temperature, H.dtype, chunk, _flags(topk_logit, accumulate))
     ws, _ = _workspace(prob, KD_OP_FUSED, workspace, H.device)
     loss = torch.empty(1, dtype=torch.float32, device=H.device) if loss is None else loss
     lse = torch.empty(T, dtype=torch.float32, device=H.device) if want_lse else None
@@ -198,9 +212,25 @@ def kd_topk_kl_fused(H, W, topk_idx, topk_logit, ignore=None, grad_loss=None, te
 def kd_topk_kl_validate(topk_idx, topk_logit, V, ignore=None, stream=None) -> torch.Tensor:
     """Device int64[1]: ids outside [0, V) plus kept rows without a finite teacher logit."""
     T, K = topk_idx.shape
-    prob = problem(T, 8, V, K, 1.0, torch.bfloat16, 0)
+    prob = problem(T, 8, V, K, 1.0, torch.bfloat16, 0, _flags(topk_logit))
     bad = torch.empty(1, dtype=torch.int64, device=topk_idx.device)
     st = load_library().kd_topk_kl_validate(ctypes.byref(prob), _ptr(topk_idx), _ptr(topk_logit), _ptr(ignore),
                                             _ptr(bad), _stream(stream))
     _check("kd_topk_kl_validate", st)
     return bad
+
+
+def kd_topk_kl_scale_grads(grad_loss, grad_H=None, grad_W=None, stream=None):
+    """grad_H and grad_W (as returned by kd_topk_kl_fused) *= grad_loss[0], in place."""
+    ref = grad_H if grad_H is not None else grad_W
+    if ref is None:
+        return
+    T, d = (grad_H.shape if grad_H is not None else (0, grad_W.shape[1]))
+    V = grad_W.shape[0] if grad_W is not None else 1
+    dt = grad_H.dtype if grad_H is not None else torch.bfloat16
+    prob = problem(T, d, V, 1, 1.0, dt, 0)
+    if grad_loss.dtype != torch.float32 or not grad_loss.is_cuda:
+        raise ValueError("grad_loss must be a float32 device tensor")
+    st = load_library().kd_topk_kl_scale_grads(ctypes.byref(prob), _ptr(grad_loss), _ptr(grad_H), _ptr(grad_W),
+                                               _stream(stream))
+    _check("kd_topk_kl_scale_grads", st)

@@ -388,7 +388,8 @@ struct RowParams {
     const void* H;          // [T][d]
     const void* W;          // [V][d]
     const int32_t* idx;     // [T][K]
-    const float* logit;     // [T][K]
+    const void* logit;      // [T][K] fp32, or bf16 when logit_bf16
+    int logit_bf16;
     const uint8_t* ignore;  // [T] or null
     const f32x2* stats;     // [C][nst]
     const float* lse_in;    // [T] (kBwd)
@@ -400,6 +401,12 @@ struct RowParams {
 };
 
 constexpr int kMaxK = 1024;
+
+// Cached teacher logit i (fp32, or bf16 widened exactly).
+__device__ __forceinline__ float teacher_logit(const void* logit, int bf16, int64_t i) {
+    return bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(logit)[i])
+                : reinterpret_cast<const float*>(logit)[i];
+}
 
 template <typename E>
 __device__ __forceinline__ float dot_row(const E* h, const E* w, int d, int lane) {
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     const int K = p.K;
     float bmax = -INFINITY;
     for (int k = tid; k < K; k += kThreads) {
-        const float b = p.logit[(int64_t)t * K + k] * p.inv_tau;
+        const float b = teacher_logit(p.logit, p.logit_bf16, (int64_t)t * K + k) * p.inv_tau;
         sh_lp[k] = b;
         sh_id[k] = clamp_id(p.idx[(int64_t)t * K + k], p.V);
         bmax = fmaxf(bmax, b);
@@ -658,7 +665,7 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(u32x4* p, int64_t n16) {
 }
 
 // Precondition check: ids outside [0, V) and kept rows without a finite teacher logit.
-__global__ __launch_bounds__(kThreads) void validate_kernel(const int32_t* idx, const float* logit,
+__global__ __launch_bounds__(kThreads) void validate_kernel(const int32_t* idx, const void* logit, int logit_bf16,
                                                             const uint8_t* ignore, int64_t T, int K, int V,
                                                             unsigned long long* bad) {
     const int64_t t = blockIdx.x;
@@ -669,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(const int32_t* idx, 
     for (int k = threadIdx.x; k < K; k += kThreads) {
         const int id = idx[t * K + k];
         nbad += (id < 0 || id >= V);
-        const float l = logit[t * K + k];
+        const float l = teacher_logit(logit, logit_bf16, t * K + k);
         nan |= (l != l);
         finite |= (l > -INFINITY && l == l);
     }
@@ -685,6 +692,24 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(const int32_t* idx, 
         for (int i = 0; i < kThreads; ++i) { f |= shf[i]; n |= shn[i]; b += shb[i]; }
         b += (!f || n) ? 1ull : 0ull;
         if (b) atomicAdd(bad, b);
+    }
+}
+
+// x *= g[0] over n16 16-byte chunks of element type E (bf16: rounded to nearest even).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void scale_kernel(u32x4* x, int64_t n16, const float* g) {
+    const float s = *g;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kThreads) {
+        u32x4 v = x[i];
+        if constexpr (Elem<E>::size == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v[q] = pack_bf16x2(bf16_bits_to_f32(v[q] & 0xFFFFu) * s, bf16_bits_to_f32(v[q] >> 16) * s);
+        } else {
+            f32x4 f = __builtin_bit_cast(f32x4, v) * s;
+            v = __builtin_bit_cast(u32x4, f);
+        }
+        x[i] = v;
     }
 }
 

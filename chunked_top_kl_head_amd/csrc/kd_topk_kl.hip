@@ -63,6 +63,8 @@ struct Plan {
     int64_t V_pad, nst;   // padded vocabulary; (max, sum) partials per row
     float tau;
     int splits;           // grad_H splits over the vocabulary
+    bool accumulate;      // grad_W += instead of =
+    bool logit_bf16;      // teacher logits are bf16
     size_t off_hdr, off_closs, off_stats, off_G, off_part, total;
 };
 
@@ -125,6 +127,7 @@ static kd_status check_problem(const kd_problem* p) {
     if (!std::isfinite(p->temperature) || !(p->temperature > 0.f)) return KD_ERR_VALUE;
     if (p->dtype != KD_BF16 && p->dtype != KD_F32) return KD_ERR_UNSUPPORTED;
     if (p->d % 8 != 0 || p->K > kMaxK || p->V > ((int64_t)1 << 21)) return KD_ERR_UNSUPPORTED;
+    if ((p->flags & ~(KD_FLAG_ACCUMULATE_GRAD_W | KD_FLAG_LOGIT_BF16)) != 0 || p->reserved != 0) return KD_ERR_VALUE;
     return KD_OK;
 }
 
@@ -136,6 +139,8 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
     q.T = p->T; q.d = p->d; q.V = p->V; q.K = p->K;
     q.es = p->dtype == KD_BF16 ? 2 : 4;
     q.tau = p->temperature;
+    q.accumulate = (p->flags & KD_FLAG_ACCUMULATE_GRAD_W) != 0;
+    q.logit_bf16 = (p->flags & KD_FLAG_LOGIT_BF16) != 0;
     q.V_pad = cdiv(q.V, BM) * BM;
     q.nst = q.V_pad / kStatIds;
     q.C = p->chunk > 0 ? p->chunk : default_chunk(q.d, q.V, q.es);
@@ -191,7 +196,7 @@ static inline Operand operand(const void* ptr, int64_t ld, int64_t bytes) {
 // One op over all chunks.  All pointers already validated.
 template <typename E>
 static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, const int32_t* idx,
-                     const float* logit, const uint8_t* ignore, const float* grad_loss, float* loss,
+                     const void* logit, const uint8_t* ignore, const float* grad_loss, float* loss,
                      const float* lse_in, float* lse_out, float* row_loss, void* grad_H, float* grad_W,
                      void* ws, hipStream_t stream) {
     char* wsb = static_cast<char*>(ws);
@@ -205,7 +210,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
     const bool want_loss = op != KD_OP_BACKWARD;
 
     hipLaunchKernelGGL(prepass_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, ignore, pl.T, grad_loss, pl.tau);
-    if (want_grads && pl.T == 0) {
+    if (want_grads && pl.T == 0 && !pl.accumulate) {
         const int64_t n16 = pl.V * pl.d * 4 / 16;
         hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(kThreads), 0, stream, reinterpret_cast<u32x4*>(grad_W), n16);
     }
@@ -239,7 +244,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             rp.t0 = (int)t0; rp.rows = (int)rc;
             rp.d = (int)pl.d; rp.V = (int)pl.V; rp.V_pad = (int)pl.V_pad; rp.K = (int)pl.K; rp.nst = (int)pl.nst;
             rp.inv_tau = 1.0f / pl.tau;
-            rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.ignore = ignore;
+            rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.logit_bf16 = pl.logit_bf16; rp.ignore = ignore;
             rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss;
             rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
             {
@@ -278,7 +283,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
             const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 8);
             GradWParams wp{};
-            wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0;
+            wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0 || pl.accumulate;
             launch_gemm<E, false, false, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp);
         }
     }
@@ -287,7 +292,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
 }
 
 static kd_status dispatch(const Plan& pl, int dtype, kd_op op, const void* H, const void* W, const int32_t* idx,
-                          const float* logit, const uint8_t* ignore, const float* grad_loss, float* loss,
+                          const void* logit, const uint8_t* ignore, const float* grad_loss, float* loss,
                           const float* lse_in, float* lse_out, float* row_loss, void* grad_H, float* grad_W,
                           void* ws, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -305,13 +310,14 @@ using namespace kd;
 
 // Common argument checks: inputs present and aligned, workspace large enough.
 static kd_status check_common(const kd_problem* p, kd_op op, const void* H, const void* W, const int32_t* idx,
-                              const float* logit, void* ws, size_t ws_bytes, Plan* pl) {
+                              const void* logit, void* ws, size_t ws_bytes, Plan* pl) {
     kd_status st = make_plan(p, op, pl);
     if (st != KD_OK) return st;
     if (!W) return KD_ERR_NULL;
     if (p->T > 0 && (!H || !idx || !logit)) return KD_ERR_NULL;
     if (pl->total > 0 && !ws) return KD_ERR_NULL;
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(ws, 16) || !aligned(idx, 4) || !aligned(logit, 4))
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(ws, 16) || !aligned(idx, 4) ||
+        !aligned(logit, pl->logit_bf16 ? 2 : 4))
         return KD_ERR_ALIGN;
     if (ws_bytes < pl->total) return KD_ERR_WORKSPACE;
     return KD_OK;
@@ -338,7 +344,7 @@ kd_status kd_topk_kl_workspace_size(const kd_problem* prob, kd_op op, size_t* by
 }
 
 kd_status kd_topk_kl_forward(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
-                             const float* topk_logit, const uint8_t* ignore, float* loss, float* lse, float* row_loss,
+                             const void* topk_logit, const uint8_t* ignore, float* loss, float* lse, float* row_loss,
                              void* workspace, size_t workspace_bytes, void* stream) {
     try {
         Plan pl;
@@ -354,7 +360,7 @@ kd_status kd_topk_kl_forward(const kd_problem* prob, const void* H, const void* 
 }
 
 kd_status kd_topk_kl_backward(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
-                              const float* topk_logit, const uint8_t* ignore, const float* lse,
+                              const void* topk_logit, const uint8_t* ignore, const float* lse,
                               const float* grad_loss, void* grad_H, float* grad_W, void* workspace,
                               size_t workspace_bytes, void* stream) {
     try {
@@ -372,7 +378,7 @@ kd_status kd_topk_kl_backward(const kd_problem* prob, const void* H, const void*
 }
 
 kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
-                           const float* topk_logit, const uint8_t* ignore, const float* grad_loss, float* loss,
+                           const void* topk_logit, const uint8_t* ignore, const float* grad_loss, float* loss,
                            float* lse, float* row_loss, void* grad_H, float* grad_W, void* workspace,
                            size_t workspace_bytes, void* stream) {
     try {
@@ -390,13 +396,14 @@ kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W,
     }
 }
 
-kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx, const float* topk_logit,
+kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx, const void* topk_logit,
                               const uint8_t* ignore, int64_t* bad_count, void* stream) {
     try {
         kd_status st = check_problem(prob);
         if (st != KD_OK) return st;
         if (!bad_count || (prob->T > 0 && (!topk_idx || !topk_logit))) return KD_ERR_NULL;
-        if (!aligned(bad_count, 8) || !aligned(topk_idx, 4) || !aligned(topk_logit, 4)) return KD_ERR_ALIGN;
+        const bool lb16 = (prob->flags & KD_FLAG_LOGIT_BF16) != 0;
+        if (!aligned(bad_count, 8) || !aligned(topk_idx, 4) || !aligned(topk_logit, lb16 ? 2 : 4)) return KD_ERR_ALIGN;
         if (prob->T > 0x7FFFFFFF) return KD_ERR_UNSUPPORTED;
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
         (void)hipGetLastError();
@@ -404,7 +411,39 @@ kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx, c
         hipLaunchKernelGGL(set_zero_u64, dim3(1), dim3(64), 0, s, bc);
         if (prob->T > 0)
             hipLaunchKernelGGL(validate_kernel, dim3((unsigned)prob->T), dim3(kThreads), 0, s, topk_idx, topk_logit,
-                               ignore, prob->T, (int)prob->K, (int)prob->V, bc);
+                               (int)lb16, ignore, prob->T, (int)prob->K, (int)prob->V, bc);
+        return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_topk_kl_scale_grads(const kd_problem* prob, const float* grad_loss, void* grad_H, float* grad_W,
+                                 void* stream) {
+    try {
+        kd_status st = check_problem(prob);
+        if (st != KD_OK) return st;
+        if (!grad_loss) return KD_ERR_NULL;
+        if (!aligned(grad_loss, 4) || !aligned(grad_H, 16) || !aligned(grad_W, 16)) return KD_ERR_ALIGN;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        (void)hipGetLastError();
+        const int es = prob->dtype == KD_BF16 ? 2 : 4;
+        if (grad_H && prob->T > 0) {
+            const int64_t n16 = prob->T * prob->d * es / 16;   // d % 8 == 0: whole 16-byte chunks
+            const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n16, kThreads), 4096);
+            if (es == 2)
+                hipLaunchKernelGGL(scale_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, s,
+                                   reinterpret_cast<u32x4*>(grad_H), n16, grad_loss);
+            else
+                hipLaunchKernelGGL(scale_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
+                                   reinterpret_cast<u32x4*>(grad_H), n16, grad_loss);
+        }
+        if (grad_W) {
+            const int64_t n16 = prob->V * prob->d * 4 / 16;
+            const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n16, kThreads), 4096);
+            hipLaunchKernelGGL(scale_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
+                               reinterpret_cast<u32x4*>(grad_W), n16, grad_loss);
+        }
         return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
     } catch (...) {
         return KD_ERR_INTERNAL;
@@ -433,7 +472,7 @@ const char* kd_status_string(kd_status status) {
         case KD_OK: return "ok";
         case KD_ERR_NULL: return "a required pointer is NULL";
         case KD_ERR_SHAPE: return "invalid shape (T, d, V, K or chunk)";
-        case KD_ERR_VALUE: return "invalid value (temperature must be finite and > 0)";
+        case KD_ERR_VALUE: return "invalid value (temperature must be finite and > 0; flags known; reserved 0)";
         case KD_ERR_ALIGN: return "misaligned pointer";
         case KD_ERR_WORKSPACE: return "workspace smaller than kd_topk_kl_workspace_size";
         case KD_ERR_UNSUPPORTED: return "unsupported problem (dtype, d % 8, K > 1024 or size limits)";

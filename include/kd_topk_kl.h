@@ -45,13 +45,14 @@
  *   H          [T, d]  element type `dtype`
  *   W          [V, d]  element type `dtype` (the nn.Linear weight layout)
  *   topk_idx   [T, K]  int32, ids in [0, V)
- *   topk_logit [T, K]  fp32 teacher logits (-inf allowed: probability 0)
+ *   topk_logit [T, K]  fp32 teacher logits (-inf allowed: probability 0), or
+ *                      bf16 bit patterns with KD_FLAG_LOGIT_BF16
  *   ignore     [T]     uint8, non-zero = position excluded; NULL = none excluded
  *   loss       [1]     fp32; lse, row_loss [T] fp32
  *   grad_H     [T, d]  element type `dtype` (rounded to nearest even from fp32), overwritten
- *   grad_W     [V, d]  fp32, overwritten
+ *   grad_W     [V, d]  fp32, overwritten (added to with KD_FLAG_ACCUMULATE_GRAD_W)
  * Alignment: H, W, grad_H, grad_W and workspace 16 bytes; the fp32/int32
- * arrays 4 bytes.  Outputs must not alias inputs or each other.
+ * arrays 4 bytes; a bf16 topk_logit 2 bytes.  Outputs must not alias inputs or each other.
  *
  * Errors.  Every argument check runs on the host before anything is enqueued;
  * on error nothing is enqueued and the outputs are untouched.  No C++
@@ -76,7 +77,7 @@ typedef enum {
     KD_OK = 0,
     KD_ERR_NULL = 1,         /* a required pointer is NULL */
     KD_ERR_SHAPE = 2,        /* T < 0, d < 1, V < 1, K < 1, K > V, chunk < 0 */
-    KD_ERR_VALUE = 3,        /* temperature not finite or <= 0 */
+    KD_ERR_VALUE = 3,        /* temperature not finite or <= 0, unknown flags, reserved != 0 */
     KD_ERR_ALIGN = 4,        /* a pointer violates the alignment above */
     KD_ERR_WORKSPACE = 5,    /* workspace_bytes below kd_topk_kl_workspace_size */
     KD_ERR_UNSUPPORTED = 6,  /* dtype unknown, d % 8 != 0, K > 1024, or sizes beyond the 2^31-byte operand limit */
@@ -88,6 +89,16 @@ typedef enum { KD_BF16 = 0, KD_F32 = 1 } kd_dtype;
 
 typedef enum { KD_OP_FORWARD = 0, KD_OP_BACKWARD = 1, KD_OP_FUSED = 2 } kd_op;
 
+/* Options (kd_problem.flags), for use inside a training step:
+ *   KD_FLAG_ACCUMULATE_GRAD_W  backward and fused add G^T H to the caller's
+ *                              grad_W instead of overwriting it (e.g. straight
+ *                              into a parameter's gradient buffer, or for an
+ *                              output projection tied to the input embedding,
+ *                              whose other gradient is already there);
+ *   KD_FLAG_LOGIT_BF16         topk_logit holds bfloat16 values (a cache of
+ *                              half the size); they are widened exactly to fp32. */
+enum { KD_FLAG_ACCUMULATE_GRAD_W = 1, KD_FLAG_LOGIT_BF16 = 2 };
+
 typedef struct {
     int64_t T;            /* positions (batch x sequence, flattened) */
     int64_t d;            /* hidden size, multiple of 8 */
@@ -96,6 +107,8 @@ typedef struct {
     int64_t chunk;        /* rows per chunk C; 0 = library default (kd_topk_kl_default_chunk) */
     int32_t dtype;        /* kd_dtype of H, W and grad_H */
     float temperature;    /* tau > 0, divides both teacher and student logits */
+    int32_t flags;        /* KD_FLAG_* bits (0 = overwrite grad_W, fp32 teacher logits); others: KD_ERR_VALUE */
+    int32_t reserved;     /* must be 0 (KD_ERR_VALUE otherwise) */
 } kd_problem;
 
 /* Chunk size used when prob->chunk == 0 (depends on d, V and dtype only). */
@@ -111,7 +124,7 @@ kd_status kd_topk_kl_workspace_size(const kd_problem* prob, kd_op op, size_t* by
  * for every position, ignored ones too) and, if non-NULL, row_loss[T] (0 on
  * ignored positions). */
 kd_status kd_topk_kl_forward(const kd_problem* prob, const void* H, const void* W,
-                             const int32_t* topk_idx, const float* topk_logit,
+                             const int32_t* topk_idx, const void* topk_logit,
                              const uint8_t* ignore, float* loss, float* lse, float* row_loss,
                              void* workspace, size_t workspace_bytes, void* stream);
 
@@ -120,7 +133,7 @@ kd_status kd_topk_kl_forward(const kd_problem* prob, const void* H, const void* 
  * grad_loss[1] (device fp32; NULL means 1).  Overwrites grad_H[T, d] and
  * grad_W[V, d]. */
 kd_status kd_topk_kl_backward(const kd_problem* prob, const void* H, const void* W,
-                              const int32_t* topk_idx, const float* topk_logit,
+                              const int32_t* topk_idx, const void* topk_logit,
                               const uint8_t* ignore, const float* lse, const float* grad_loss,
                               void* grad_H, float* grad_W,
                               void* workspace, size_t workspace_bytes, void* stream);
@@ -129,7 +142,7 @@ kd_status kd_topk_kl_backward(const kd_problem* prob, const void* H, const void*
  * projected once and reused for the loss and the gradients).  Same outputs as
  * the two calls above; lse and row_loss may be NULL. */
 kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W,
-                           const int32_t* topk_idx, const float* topk_logit,
+                           const int32_t* topk_idx, const void* topk_logit,
                            const uint8_t* ignore, const float* grad_loss,
                            float* loss, float* lse, float* row_loss,
                            void* grad_H, float* grad_W,
@@ -139,8 +152,18 @@ kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W,
  * int64) the number of ids outside [0, V) plus the number of kept positions
  * whose teacher logits are all -inf or contain NaN. */
 kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx,
-                              const float* topk_logit, const uint8_t* ignore,
+                              const void* topk_logit, const uint8_t* ignore,
                               int64_t* bad_count, void* stream);
+
+/* Multiplies grad_H[T, d] (element type `dtype`, rounded to nearest even)
+ * and grad_W[V, d] (fp32) in place by the device scalar grad_loss[0].  For
+ * callers that run kd_topk_kl_fused with grad_loss = NULL (g = 1) before the
+ * upstream gradient is known -- an autograd function whose forward already
+ * produced the gradients -- and apply g afterwards: G above, and so both
+ * gradients, are proportional to g.  Either pointer may be NULL to skip that
+ * array; grad_W must not hold other accumulated gradients. */
+kd_status kd_topk_kl_scale_grads(const kd_problem* prob, const float* grad_loss, void* grad_H, float* grad_W,
+                                 void* stream);
 
 /* Kernel stages of every call, for timing. */
 typedef enum {

@@ -169,6 +169,45 @@ def test_validate_argument_errors(lib):
     assert lib.kd_topk_kl_validate(ctypes.byref(p), P4, P4, None, P4, None) == B.KD_ERR_ALIGN
 
 
+def test_problem_struct_layout():
+    # int64 T, d, V, K, chunk; int32 dtype; float temperature; int32 flags, reserved
+    assert ctypes.sizeof(B.KdProblem) == 56
+    assert B.KdProblem.flags.offset == 48 and B.KdProblem.reserved.offset == 52
+
+
+@pytest.mark.parametrize("flags,reserved,status", [
+    (B.KD_FLAG_ACCUMULATE_GRAD_W, 0, B.KD_OK), (B.KD_FLAG_LOGIT_BF16, 0, B.KD_OK),
+    (B.KD_FLAG_ACCUMULATE_GRAD_W | B.KD_FLAG_LOGIT_BF16, 0, B.KD_OK),
+    (4, 0, B.KD_ERR_VALUE), (1 << 30, 0, B.KD_ERR_VALUE), (0, 1, B.KD_ERR_VALUE),
+])
+def test_flags_validation(lib, flags, reserved, status):
+    p = prob()
+    p.flags, p.reserved = flags, reserved
+    assert ws_size(lib, p, B.KD_OP_FUSED)[0] == status
+
+
+def test_bf16_logit_alignment(lib):
+    p = prob()
+    p.flags = B.KD_FLAG_LOGIT_BF16
+    odd = ctypes.c_void_p(0x500001)
+    assert call_fwd(lib, p, lg=odd) == B.KD_ERR_ALIGN
+    assert call_bwd(lib, p, lg=odd) == B.KD_ERR_ALIGN
+    assert call_fused(lib, p, lg=odd) == B.KD_ERR_ALIGN
+    assert lib.kd_topk_kl_validate(ctypes.byref(p), P4, odd, None, P16, None) == B.KD_ERR_ALIGN
+    # a 2-byte aligned fp32 cache is rejected
+    assert call_fwd(lib, prob(), lg=MIS) == B.KD_ERR_ALIGN
+
+
+def test_scale_grads_argument_errors(lib):
+    p = prob()
+    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), None, P16, P16b, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), MIS, P16, P16b, None) == B.KD_ERR_ALIGN
+    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), P4, P4, P16b, None) == B.KD_ERR_ALIGN
+    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), P4, P16, P4, None) == B.KD_ERR_ALIGN
+    assert lib.kd_topk_kl_scale_grads(ctypes.byref(prob(tau=0.0)), P4, P16, P16b, None) == B.KD_ERR_VALUE
+    assert lib.kd_topk_kl_scale_grads(None, P4, P16, P16b, None) == B.KD_ERR_NULL
+
+
 def test_status_strings(lib):
     for s in range(9):
         msg = lib.kd_status_string(s).decode()
