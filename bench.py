@@ -30,7 +30,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "fwd+bwd tokens/s of fused top-K KL loss; MFMA util % of bf16 peak; peak HBM GiB"
-KERNEL_SOURCES = ("kd_common.hpp", "kd_gemm.hpp", "kd_gemm_dtl.hpp", "kd_kernels.hpp", "kd_topk_kl.hip")
+KERNEL_SOURCES = ("kd_common.hpp", "kd_gemm.hpp", "kd_gemm_dtl.hpp", "kd_kernels.hpp", "kd_topk_select.hpp",
+                  "kd_topk_kl.hip")
 
 
 def kernel_source_hash() -> str:
@@ -85,6 +86,59 @@ def cpu_baseline(x, rows: int) -> dict:
                       f"fp64, {dt:.1f} s"}
 
 
+def bench_select(args) -> int:
+    """The teacher top-K cache producer (kd_topk_select) on the teacher logits of
+    the GPT-OSS-like workload: T = 32768 rows of V = 201088 bf16 logits, K = 100.
+    One step = one call over all rows; prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from chunked_top_kl_head_amd import binding as B
+
+    T, V, K = 32768, 201088, 100
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261203)
+    logits = (torch.randn(T, V, device=dev, generator=g) * 3).to(torch.bfloat16)
+    for _ in range(args.warmup):
+        B.kd_topk_select(logits, K)
+    ev = HipEvents()
+    whole = ev.create(2)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    ev.rt.hipEventRecord(ctypes.c_void_p(whole[0]), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        idx, val = B.kd_topk_select(logits, K)
+    ev.rt.hipEventRecord(ctypes.c_void_p(whole[1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(whole[0], whole[1]) / args.steps
+    ev.destroy(whole)
+    algo_bytes = T * V * 2 + T * K * 8           # read the logits once, write ids + fp32 logits
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "teacher top-K cache rows/s (per-row top-100 of bf16 logits)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (3 * N(0,1) logits)",
+        "config": {"workload": f"topk_select: T={T} V={V} K={K} bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "topk_select"},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.topk_select import topk_select
+
+        rows = min(args.cpu_rows, T)
+        sub = logits[:rows].float().cpu().numpy()
+        t0 = time.perf_counter()
+        topk_select(sub, K)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {rows} rows, numpy lexsort per row, {dt:.1f} s"}
+    del np
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     from chunked_top_kl_head_amd import synth
 
@@ -98,6 +152,8 @@ def main() -> int:
                     help="fused entry, or forward followed by backward")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select", action="store_true",
+                    help="benchmark the teacher top-K cache producer instead of the loss")
     ap.add_argument("--copy-calibration-bytes", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many bytes (a kernel of known "
                          "traffic, used to scale the FETCH_SIZE/WRITE_SIZE counters of a profiling run)")
@@ -117,6 +173,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.select:
+        return bench_select(args)
     wl = synth.WORKLOADS[args.workload]
     chunk = args.chunk or wl.chunk
     t_gen = time.perf_counter()

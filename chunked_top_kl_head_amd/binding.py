@@ -33,6 +33,7 @@ EXPORTS = (
     "kd_topk_kl_scale_grads",
     "kd_topk_kl_set_stage_events",
     "kd_status_string",
+    "kd_topk_select",
 )
 KD_STAGE_LOGITS, KD_STAGE_ROWS, KD_STAGE_GRAD_H, KD_STAGE_GRAD_W = 0, 1, 2, 3
 STAGE_NAMES = ("logits", "rows", "grad_H", "grad_W")
@@ -42,6 +43,11 @@ class KdProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32), ("temperature", ctypes.c_float),
                 ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class KdSelectProblem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int64), ("ld", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class KdError(RuntimeError):
@@ -80,6 +86,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kd_topk_kl_scale_grads.restype = ctypes.c_int
     lib.kd_topk_kl_set_stage_events.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.kd_topk_kl_set_stage_events.restype = ctypes.c_int
+    lib.kd_topk_select.argtypes = [ctypes.POINTER(KdSelectProblem), vp, vp, vp, vp]
+    lib.kd_topk_select.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -234,3 +242,24 @@ def kd_topk_kl_scale_grads(grad_loss, grad_H=None, grad_W=None, stream=None):
     st = load_library().kd_topk_kl_scale_grads(ctypes.byref(prob), _ptr(grad_loss), _ptr(grad_H), _ptr(grad_W),
                                                _stream(stream))
     _check("kd_topk_kl_scale_grads", st)
+
+
+def kd_topk_select(logits, K: int, V: Optional[int] = None, stream=None):
+    """Per row of logits [T, ld] (bf16 or fp32, device), the K largest of the first V values:
+    returns (topk_idx int32 [T, K], topk_logit fp32 [T, K]), descending, equal values by id."""
+    if not logits.is_cuda or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D device tensor with unit column stride")
+    if logits.dtype == torch.bfloat16:
+        dt = KD_BF16
+    elif logits.dtype == torch.float32:
+        dt = KD_F32
+    else:
+        raise ValueError(f"unsupported dtype {logits.dtype}")
+    T, n = logits.shape
+    V = n if V is None else int(V)
+    prob = KdSelectProblem(int(T), V, int(K), int(logits.stride(0)), dt, 0)
+    idx = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    val = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    st = load_library().kd_topk_select(ctypes.byref(prob), _ptr(logits), _ptr(idx), _ptr(val), _stream(stream))
+    _check("kd_topk_select", st)
+    return idx, val

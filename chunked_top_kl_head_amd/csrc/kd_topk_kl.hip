@@ -25,7 +25,9 @@
 #include <cstring>
 
 #include "kd_kernels.hpp"
+#include "kd_topk_select.hpp"
 #include "kd_topk_kl.h"
+#include "kd_topk_select.h"
 
 namespace kd {
 
@@ -444,6 +446,33 @@ kd_status kd_topk_kl_scale_grads(const kd_problem* prob, const float* grad_loss,
             hipLaunchKernelGGL(scale_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
                                reinterpret_cast<u32x4*>(grad_W), n16, grad_loss);
         }
+        return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_topk_select(const kd_select_problem* prob, const void* logits, int32_t* topk_idx, float* topk_logit,
+                         void* stream) {
+    try {
+        if (!prob) return KD_ERR_NULL;
+        const kd_select_problem& p = *prob;
+        if (p.T < 0 || p.V < 1 || p.K < 1 || p.K > p.V || p.ld < p.V) return KD_ERR_SHAPE;
+        if (p.reserved != 0) return KD_ERR_VALUE;
+        if ((p.dtype != KD_BF16 && p.dtype != KD_F32) || p.K > kSelMaxK || p.V > 0x7FFFFFFF || p.T > 0x7FFFFFFF)
+            return KD_ERR_UNSUPPORTED;
+        if (p.T == 0) return KD_OK;
+        if (!logits || !topk_idx || !topk_logit) return KD_ERR_NULL;
+        const int es = p.dtype == KD_BF16 ? 2 : 4;
+        if (!aligned(logits, es) || !aligned(topk_idx, 4) || !aligned(topk_logit, 4)) return KD_ERR_ALIGN;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        (void)hipGetLastError();
+        if (es == 2)
+            hipLaunchKernelGGL(topk_select_kernel<bf16_t>, dim3((unsigned)p.T), dim3(kSelThreads), 0, s, logits, p.ld,
+                               (int)p.V, (int)p.K, topk_idx, topk_logit);
+        else
+            hipLaunchKernelGGL(topk_select_kernel<float>, dim3((unsigned)p.T), dim3(kSelThreads), 0, s, logits, p.ld,
+                               (int)p.V, (int)p.K, topk_idx, topk_logit);
         return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
     } catch (...) {
         return KD_ERR_INTERNAL;

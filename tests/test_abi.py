@@ -9,7 +9,7 @@ import pytest
 from chunked_top_kl_head_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kd_topk_kl.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("kd_topk_kl.h", "kd_topk_select.h")]
 
 # fake but well-aligned device addresses: validation never dereferences them
 P16 = ctypes.c_void_p(0x100000)
@@ -27,8 +27,12 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:kd_status|size_t|int64_t|const char\*)\s+(kd_\w+)\s*\(", text, re.M)))
+
+
+def test_every_header_in_include_is_checked():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == sorted(os.path.basename(h) for h in HEADERS)
 
 
 def test_header_declarations_match_binding():
@@ -213,3 +217,35 @@ def test_status_strings(lib):
         msg = lib.kd_status_string(s).decode()
         assert msg and msg != "unknown status"
     assert lib.kd_status_string(99).decode() == "unknown status"
+
+
+def sel(T=4, V=1000, K=10, ld=None, dtype=B.KD_BF16, reserved=0):
+    return B.KdSelectProblem(T, V, K, V if ld is None else ld, dtype, reserved)
+
+
+def test_select_struct_layout():
+    assert ctypes.sizeof(B.KdSelectProblem) == 40
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), B.KD_ERR_SHAPE), (dict(V=0), B.KD_ERR_SHAPE), (dict(K=0), B.KD_ERR_SHAPE),
+    (dict(K=1001), B.KD_ERR_SHAPE), (dict(ld=999), B.KD_ERR_SHAPE), (dict(reserved=3), B.KD_ERR_VALUE),
+    (dict(dtype=5), B.KD_ERR_UNSUPPORTED), (dict(V=5000, K=1025), B.KD_ERR_UNSUPPORTED),
+    (dict(V=1 << 31, K=10), B.KD_ERR_UNSUPPORTED),
+])
+def test_select_validation(lib, kw, status):
+    assert lib.kd_topk_select(ctypes.byref(sel(**kw)), P16, P4, P4, None) == status
+
+
+def test_select_argument_errors(lib):
+    p = sel()
+    assert lib.kd_topk_select(None, P16, P4, P4, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_select(ctypes.byref(p), None, P4, P4, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_select(ctypes.byref(p), P16, None, P4, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_select(ctypes.byref(p), P16, P4, None, None) == B.KD_ERR_NULL
+    assert lib.kd_topk_select(ctypes.byref(p), ctypes.c_void_p(0x100001), P4, P4, None) == B.KD_ERR_ALIGN
+    assert lib.kd_topk_select(ctypes.byref(sel(dtype=B.KD_F32)), MIS, P4, P4, None) == B.KD_ERR_ALIGN
+    assert lib.kd_topk_select(ctypes.byref(p), P16, MIS, P4, None) == B.KD_ERR_ALIGN
+    assert lib.kd_topk_select(ctypes.byref(p), P16, P4, MIS, None) == B.KD_ERR_ALIGN
+    # no rows: nothing to do, nothing dereferenced
+    assert lib.kd_topk_select(ctypes.byref(sel(T=0)), None, None, None, None) == B.KD_OK

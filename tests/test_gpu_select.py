@@ -1,0 +1,96 @@
+"""GPU parity of the teacher top-K cache producer (kd_topk_select) against the
+oracle (oracle/topk_select.py): ids and values bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_top_kl_head_amd import binding as B
+from oracle.topk_select import topk_select
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_and_compare(x: np.ndarray, K: int, dtype, ld=None):
+    """x: fp32 values (already bf16-representable when dtype is bf16)."""
+    T, V = x.shape
+    pitch = V if ld is None else ld
+    host = np.zeros((T, pitch), dtype=np.float32)
+    host[:, V:] = np.inf            # padding beyond V must never be selected
+    host[:, :V] = x
+    dev = torch.from_numpy(host).cuda().to(dtype)
+    idx, val = B.kd_topk_select(dev, K, V=V)
+    torch.cuda.synchronize()
+    ref_idx, ref_val = topk_select(x, K)
+    got_idx = idx.cpu().numpy()
+    got_val = val.cpu().numpy()
+    assert np.array_equal(got_idx, ref_idx)
+    # values bit for bit (signed zeros included); a selected NaN is some NaN
+    nan = np.isnan(ref_val)
+    assert np.array_equal(np.isnan(got_val), nan)
+    assert np.array_equal(got_val[~nan].view(np.uint32), ref_val[~nan].view(np.uint32))
+
+
+def bf16_values(a: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("V,K", [(37, 1), (37, 37), (1000, 100), (5003, 100), (5003, 1024), (20000, 100)])
+def test_random_rows(dtype, V, K):
+    rng = np.random.default_rng(V * 7 + K)
+    x = (rng.standard_normal((48, V)) * 3).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = bf16_values(x)
+    say(f"V={V} K={K} {dtype}")
+    run_and_compare(x, K, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_special_rows(dtype):
+    """Ties (candidate overflow: the exact path), sorted rows, constant rows,
+    -inf, NaN and signed zeros, and a row pitch beyond V."""
+    rng = np.random.default_rng(5)
+    V = 4100
+    rows = [
+        rng.integers(0, 4, V).astype(np.float32),                   # 4 distinct values: heavy ties
+        np.sort(rng.standard_normal(V)).astype(np.float32),        # ascending
+        -np.sort(-rng.standard_normal(V)).astype(np.float32),      # descending
+        np.zeros(V, np.float32),                                   # constant
+        np.full(V, -np.inf, np.float32),
+    ]
+    r = rng.standard_normal(V).astype(np.float32)
+    r[::5] = -np.inf
+    r[2::9] = np.nan
+    r[10], r[11], r[12] = 0.0, -0.0, 0.0
+    rows.append(r)
+    x = np.stack(rows)
+    if dtype == torch.bfloat16:
+        x = bf16_values(x)
+    for K in (1, 100, 1024, V):
+        if K <= 1024:
+            run_and_compare(x, K, dtype)
+    run_and_compare(x, 100, dtype, ld=V + 60)
+
+
+def test_full_size_teacher_cache():
+    """The 32,768 x 201,088 bf16 teacher logits of the GPT-OSS-like workload,
+    K = 100: sampled rows against the oracle, every row checked for order."""
+    T, V, K = 32768, 201088, 100
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    logits = (torch.randn(T, V, device="cuda", generator=g) * 3).to(torch.bfloat16)
+    idx, val = B.kd_topk_select(logits, K)
+    torch.cuda.synchronize()
+    # every row: descending, values are the logits at the ids
+    assert bool((val[:, 1:] <= val[:, :-1]).all())
+    assert torch.equal(torch.gather(logits, 1, idx.long()).float(), val)
+    rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(1).choice(T, 29, replace=False)]))
+    sub = logits[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    ref_idx, ref_val = topk_select(sub, K)
+    assert np.array_equal(idx[torch.from_numpy(rows).cuda()].cpu().numpy(), ref_idx)
+    assert np.array_equal(val[torch.from_numpy(rows).cuda()].cpu().numpy(), ref_val)
+    say(f"  {rows.size} sampled rows exact; all {T} rows ordered")
