@@ -39,6 +39,7 @@ struct Operand {
     const void* ptr;   // element (m, k) at ptr + (kmajor ? m*ld + k : k*ld + m)
     int64_t ld;        // leading dimension, elements
     uint64_t bytes;    // readable bytes from ptr (loads beyond return 0)
+    uint64_t kblock;   // blocked operands only: bytes from one 64-wide block to the next
 };
 
 struct GemmGeom {

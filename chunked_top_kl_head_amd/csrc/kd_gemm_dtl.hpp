@@ -126,13 +126,17 @@ __device__ __forceinline__ int mn_off(int k, int m) {
 constexpr int kLoaderWaves = KD_LOADER_WAVES;
 static_assert(kLoaderWaves == 4 || kLoaderWaves == 8, "loader waves");
 
-template <int ROWS, bool KMAJOR> struct DtlLoader;
+// BLOCKED operands are stored in blocks of 64 along one dimension with the
+// other dimension's rows 128 bytes apart inside a block (Operand::kblock bytes
+// from block to block): K-contiguous blocked = 64 k of every row per block (the
+// K step reads one block); MN-contiguous blocked = 64 m of every k per block.
+template <int ROWS, bool KMAJOR, bool BLOCKED = false> struct DtlLoader;
 
 // K-contiguous operand.  Load instruction i of loader wave w covers tile rows
 // 8 u .. 8 u + 7 (u = w NI + i); lane l reads logical chunk
 // (l & 7) ^ (l >> 3) ^ (u & 7) of row 8 u + (l >> 3), which lands in the
 // swizzled slot l & 7 of that row.
-template <int ROWS> struct DtlLoader<ROWS, true> {
+template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, true, BLOCKED> {
     static_assert(ROWS == 256 && kRowBytes == 128, "tile rows and K step");
     static constexpr int NI = kDtlTile / 1024 / kLoaderWaves;
     Operand op;
@@ -146,7 +150,11 @@ template <int ROWS> struct DtlLoader<ROWS, true> {
         lrow = (uint32_t)(2 * (lane >> 3) * o.ld);
         zl = (lane & 7) ^ (lane >> 3) ^ ((wave * NI) & 7);
     }
-    __device__ __forceinline__ u32x4 rsrc(int k0) const { return window_rsrc(op, tile_off + (uint64_t)k0 * 2u); }
+    __device__ __forceinline__ u32x4 rsrc(int k0) const {
+        // blocked: ld = 64 and the step's 64 k are block k0 / 64
+        if constexpr (BLOCKED) return window_rsrc(op, tile_off + (uint64_t)(k0 >> 6) * op.kblock);
+        else return window_rsrc(op, tile_off + (uint64_t)k0 * 2u);
+    }
     __device__ __forceinline__ void hide() {
         opaque(lrow);
         opaque(zl);
@@ -180,8 +188,11 @@ template <int ROWS> struct DtlLoader<ROWS, true> {
 // MN-contiguous operand.  Load instruction i of loader wave w covers k-rows
 // 2 u and 2 u + 1 (u = w NI + i); lane l reads the 16 bytes of k-row
 // 2 u + (l >> 5) whose chunk lands in slot l & 31 of that row.
-template <int ROWS> struct DtlLoader<ROWS, false> {
+template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, false, BLOCKED> {
     static_assert(ROWS == 256, "MN-contiguous tiles are 256 wide (512-byte k-rows)");
+    // bytes between consecutive k-rows, and from one 8-chunk (64-element) group
+    // of a k-row to the next
+    __device__ __forceinline__ uint64_t krow() const { return BLOCKED ? 128u : (uint64_t)op.ld * 2u; }
     static constexpr int NI = kDtlTile / 1024 / kLoaderWaves;
     Operand op;
     uint64_t tile_off;   // byte offset of the tile's first column at this wave's first k-row
@@ -192,15 +203,14 @@ template <int ROWS> struct DtlLoader<ROWS, false> {
 
     __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
         op = o;
-        tile_off = (uint64_t)m0 * 2u + (uint64_t)(wave * NI) * 4u * (uint64_t)o.ld;
+        if constexpr (BLOCKED) tile_off = (uint64_t)(m0 >> 6) * o.kblock + (uint64_t)(wave * NI) * 2u * 128u;
+        else tile_off = (uint64_t)m0 * 2u + (uint64_t)(wave * NI) * 4u * (uint64_t)o.ld;
         kl = lane >> 5;
-        lrow = (uint32_t)(2 * kl * o.ld);
+        lrow = (uint32_t)(kl * krow());
         zl = (lane & 31) ^ (kl << 2);
         kw = (wave * NI) >> 2;
     }
-    __device__ __forceinline__ u32x4 rsrc(int k0) const {
-        return window_rsrc(op, tile_off + (uint64_t)k0 * (uint64_t)op.ld * 2u);
-    }
+    __device__ __forceinline__ u32x4 rsrc(int k0) const { return window_rsrc(op, tile_off + (uint64_t)k0 * krow()); }
     __device__ __forceinline__ void hide() {
         opaque(lrow);
         opaque(zl);
@@ -209,7 +219,11 @@ template <int ROWS> struct DtlLoader<ROWS, false> {
     __device__ __forceinline__ void issue1(const u32x4& rs, uint32_t tile, int i, int k0, int kend, bool full,
                                            int wave) const {
         const int c = zl ^ (8 * (i & 1)) ^ (16 * ((kw + (i >> 2)) & 1));
-        uint32_t v = lrow + (uint32_t)(i * 4 * op.ld) + (uint32_t)(c << 4);
+        uint32_t v;
+        if constexpr (BLOCKED)
+            v = lrow + (uint32_t)(i * 2 * 128) + (uint32_t)(c >> 3) * (uint32_t)op.kblock + (uint32_t)((c & 7) << 4);
+        else
+            v = lrow + (uint32_t)(i * 4 * op.ld) + (uint32_t)(c << 4);
         if (!full && k0 + (wave * NI + i) * 2 + kl >= kend) v = kOOB;
         dtl_load16(rs, tile + (uint32_t)((wave * NI + i) * 1024), v);
     }
@@ -268,13 +282,13 @@ constexpr int kDtlLds = 2 * kDtlStage;
 // the first two MFMA groups after that barrier, into the stage every wave has
 // just finished reading, and are awaited at the end of step it.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool B_BLOCKED, class Epi>
 __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B, const GemmGeom& g,
                                               const typename Epi::Params& ep, lds_t* smem) {
     static_assert(BM == 256 && BN == 256, "tile shape");
     constexpr int BK = kDtlBK;
     using LA = DtlLoader<BM, A_KMAJOR>;
-    using LB = DtlLoader<BN, B_KMAJOR>;
+    using LB = DtlLoader<BN, B_KMAJOR, B_BLOCKED>;
     using Mma = DtlMma<BM, BN>;
     constexpr int FM = Mma::FM, FN = Mma::FN;
     constexpr int NT = LA::NI + LB::NI;          // load instructions per step and loader wave

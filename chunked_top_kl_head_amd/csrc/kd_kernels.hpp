@@ -28,6 +28,20 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) <= 256, "header slot");
 
+// Layout of a chunk's G (and of the softmax numerators it is built from).
+// bf16: blocked by 64 vocabulary ids -- element (r, v) at ((v / 64) C + r) 64 +
+// v % 64 -- so that a gradient-GEMM K step (64 ids of 256 consecutive rows, or
+// 64 rows of 256 ids) reads contiguous 128-byte rows instead of rows 400 KB
+// apart.  fp32 (the small-problem engine): row-major [C][V_pad].
+constexpr int kGBlock = 64;
+template <typename E> struct GLayout {
+    static constexpr bool kBlocked = Elem<E>::size == 2;
+    static __device__ __forceinline__ int64_t index(int64_t r, int64_t v, int64_t C, int64_t V_pad) {
+        if constexpr (kBlocked) return ((v >> 6) * C + r) * kGBlock + (v & (kGBlock - 1));
+        else return r * V_pad + v;
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Logit-tile epilogue: the tile is Z^T (rows = vocabulary ids v, columns =
 // chunk rows t).  Each wave reduces its own 128 ids of a column to a partial
@@ -42,8 +56,8 @@ constexpr int kStatIds = 128;   // vocabulary ids per (max, sum) partial
 // ---------------------------------------------------------------------------
 struct LogitsParams {
     f32x2* stats;          // [C][nst] (max2, sum) per (row, 128-id block)
-    void* E;               // [C][V_pad] element type of the operands
-    int V, V_pad, nst, rows;
+    void* E;               // C x V_pad, GLayout<E>, element type of the operands
+    int V, V_pad, nst, rows, C;
     float scale2;          // log2(e) / tau
     const float* lse;      // kBwd: natural-log lse of the chunk rows
     const uint8_t* ignore; // kBwd: ignore flags of the chunk rows (may be null)
@@ -65,18 +79,20 @@ __device__ __forceinline__ void stage_write4(lds_t* st, int wm, int wn, int i, i
     *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(st + stage_off(t, v >> 3) + ((v & 4) << 1)) = w;
 }
 
-// Writes the staged 256 x 256 tile: rows t < rows of dst (row pitch ld
-// elements, first element at column v0), two rows per wave instruction.
-__device__ __forceinline__ void stage_flush(const lds_t* st, uint16_t* dst, int64_t ld, int n0, int v0, int rows,
+// Writes the staged 256 x 256 tile into the blocked bf16 G layout (C rows per
+// 64-id block): rows t < rows, columns v0 .. v0 + 255; every 8 lanes write one
+// whole 128-byte row segment of a block.
+__device__ __forceinline__ void stage_flush(const lds_t* st, uint16_t* dst, int64_t C, int n0, int v0, int rows,
                                             int tid) {
     const int wave = tid >> 6, lane = tid & 63;
     const int c = lane & 31;
+    const int64_t blk = (int64_t)(v0 / kGBlock + (c >> 3)) * C;
 #pragma unroll 4
     for (int k = 0; k < 16; ++k) {
         const int tl = wave * 32 + 2 * k + (lane >> 5);
         const u32x4 val = lds_read16(st, stage_off(tl, c));
         const int t = n0 + tl;
-        if (t < rows) *reinterpret_cast<u32x4*>(dst + (int64_t)t * ld + v0 + c * 8) = val;
+        if (t < rows) *reinterpret_cast<u32x4*>(dst + (blk + t) * kGBlock + (c & 7) * 8) = val;
     }
 }
 
@@ -89,9 +105,9 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                                                   float x2, float x3) {
         if constexpr (Elem<E>::size == 2) {
             u32x2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.E) + (int64_t)t * p.V_pad + v0) = w;
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.E) + GLayout<E>::index(t, v0, p.C, p.V_pad)) = w;
         } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.E) + (int64_t)t * p.V_pad + v0) =
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.E) + GLayout<E>::index(t, v0, p.C, p.V_pad)) =
                 f32x4{x0, x1, x2, x3};
         }
     }
@@ -139,7 +155,7 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
             }
             if constexpr (kStaged) {
                 __syncthreads();
-                stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.V_pad, n0, m0, p.rows, tid);
+                stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.C, n0, m0, p.rows, tid);
             }
             return;
         } else {
@@ -180,7 +196,7 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                                                   mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
                                                   mma.acc[i][j][4 * q + 3]);
                     __syncthreads();
-                    stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.V_pad, n0, m0, p.rows, tid);
+                    stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.C, n0, m0, p.rows, tid);
                 } else {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(WsHeader* hdr, const 
 struct RowParams {
     int mode;
     int t0, rows;
-    int d, V, V_pad, K, nst;
+    int d, V, V_pad, K, nst, C;
     float inv_tau;
     const void* H;          // [T][d]
     const void* W;          // [V][d]
@@ -396,7 +412,7 @@ struct RowParams {
     float* lse_out;         // [T] or null
     float* row_loss;        // [T] or null
     float* chunk_loss;      // [C]
-    void* G;                // [C][V_pad]
+    void* G;                // C x V_pad, GLayout<E>
     const WsHeader* hdr;
 };
 
@@ -490,7 +506,12 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
         lse2 = p.lse_in[t] * kLog2e;
     }
 
-    const int64_t grow = (int64_t)r * p.V_pad;
+    // 16-byte chunk c of this row of G (16 / sizeof(E) ids, never across a block)
+    constexpr int kEpc = 16 / Elem<E>::size;
+    auto gchunk = [&](int c) {
+        return reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.G) +
+                                        GLayout<E>::index(r, (int64_t)c * kEpc, p.C, p.V_pad) * Elem<E>::size);
+    };
     if (!kept) {
         if (p.mode != kBwd) {
             if (tid == 0) {
@@ -499,9 +520,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
             }
         }
         if (p.mode == kFused) {
-            u32x4* g = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.G) + grow * Elem<E>::size);
-            const int nch = p.V_pad * Elem<E>::size / 16;
-            for (int c = tid; c < nch; c += kThreads) g[c] = u32x4{0u, 0u, 0u, 0u};
+            const int nch = p.V_pad / kEpc;
+            for (int c = tid; c < nch; c += kThreads) *gchunk(c) = u32x4{0u, 0u, 0u, 0u};
         }
         return;
     }
@@ -567,7 +587,6 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
         __syncthreads();
         if constexpr (Elem<E>::size == 2) {
             // U chunks per thread in flight: the row is a pure stream
-            u32x4* g = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.G) + grow);
             const int nch = p.V_pad / 8;
             constexpr int U = 8;
             auto scale = [&](u32x4& v, int c) {
@@ -580,24 +599,24 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
             for (; c + (U - 1) * kThreads < nch; c += U * kThreads) {
                 u32x4 v[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = g[c + u * kThreads];
+                for (int u = 0; u < U; ++u) v[u] = *gchunk(c + u * kThreads);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     scale(v[u], c + u * kThreads);
-                    g[c + u * kThreads] = v[u];
+                    *gchunk(c + u * kThreads) = v[u];
                 }
             }
             for (; c < nch; c += kThreads) {
-                u32x4 v = g[c];
+                u32x4 v = *gchunk(c);
                 scale(v, c);
-                g[c] = v;
+                *gchunk(c) = v;
             }
         } else {
-            f32x4* g = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.G) + grow);
             const int nch = p.V_pad / 4;
             for (int c = tid; c < nch; c += kThreads) {
                 const float f = dyn[(c * 4) / kStatIds];
-                g[c] = g[c] * f;
+                f32x4* g = reinterpret_cast<f32x4*>(gchunk(c));
+                *g = *g * f;
             }
         }
         __syncthreads();
@@ -614,9 +633,10 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
         const float q = fast_exp2(sh_a[k] * kLog2e - lse2);
         const float gval = s * (q - P);
         if constexpr (Elem<E>::size == 2) {
-            reinterpret_cast<uint16_t*>(p.G)[grow + id] = (uint16_t)(pack_bf16x2(gval, 0.f) & 0xFFFFu);
+            reinterpret_cast<uint16_t*>(p.G)[GLayout<E>::index(r, id, p.C, p.V_pad)] =
+                (uint16_t)(pack_bf16x2(gval, 0.f) & 0xFFFFu);
         } else {
-            reinterpret_cast<float*>(p.G)[grow + id] = gval;
+            reinterpret_cast<float*>(p.G)[GLayout<E>::index(r, id, p.C, p.V_pad)] = gval;
         }
     }
 }

@@ -41,20 +41,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Operand A, Operand B, Ge
     gemm_body<E, BM, BN, AK, BK, Epi>(A, B, g, ep, (lds_t*)smem);
 }
 
-// bf16 operands: direct-to-LDS engine (8 waves, 32x32x16 bf16 MFMA)
-template <bool AK, bool BK, class Epi>
+// bf16 operands: direct-to-LDS engine (8 waves, 32x32x16 bf16 MFMA); BB: B is
+// the chunk's G in its blocked layout
+template <bool AK, bool BK, bool BB, class Epi>
 __global__ __launch_bounds__(kDtlThreads) void gemm_kernel_dtl(Operand A, Operand B, GemmGeom g,
                                                                typename Epi::Params ep) {
     __shared__ __attribute__((aligned(1024))) char smem[kDtlLds];
-    gemm_body_dtl<BM, BN, AK, BK, Epi>(A, B, g, ep, (lds_t*)smem);
+    gemm_body_dtl<BM, BN, AK, BK, BB, Epi>(A, B, g, ep, (lds_t*)smem);
 }
 
 // Launch of one contraction on the engine that matches the element type.
-template <typename E, bool AK, bool BK, class Epi>
+// BB: B is the chunk's G (blocked in the bf16 layout, row-major for fp32).
+template <typename E, bool AK, bool BK, bool BB, class Epi>
 static void launch_gemm(dim3 grid, hipStream_t stream, const Operand& A, const Operand& B, const GemmGeom& g,
                         const typename Epi::Params& ep) {
     if constexpr (Elem<E>::size == 2)
-        hipLaunchKernelGGL((gemm_kernel_dtl<AK, BK, Epi>), grid, dim3(kDtlThreads), 0, stream, A, B, g, ep);
+        hipLaunchKernelGGL((gemm_kernel_dtl<AK, BK, BB, Epi>), grid, dim3(kDtlThreads), 0, stream, A, B, g, ep);
     else
         hipLaunchKernelGGL((gemm_kernel<E, AK, BK, Epi>), grid, dim3(kThreads), 0, stream, A, B, g, ep);
 }
@@ -191,8 +193,20 @@ static dim3 gemm_grid(const GemmGeom& g, int splits) {
 
 static inline Operand operand(const void* ptr, int64_t ld, int64_t bytes) {
     Operand o;
-    o.ptr = ptr; o.ld = ld; o.bytes = (uint64_t)bytes;
+    o.ptr = ptr; o.ld = ld; o.bytes = (uint64_t)bytes; o.kblock = 0;
     return o;
+}
+
+// The chunk's G as an operand: blocked (bf16; ld 64 inside a block of C rows)
+// or row-major [C][V_pad] (fp32).
+static inline Operand g_operand(const void* G, const Plan& pl) {
+    const int64_t bytes = pl.C * pl.V_pad * pl.es;
+    if (pl.es == 2) {
+        Operand o = operand(G, kGBlock, bytes);
+        o.kblock = (uint64_t)pl.C * kGBlock * 2u;
+        return o;
+    }
+    return operand(G, pl.V_pad, bytes);
 }
 
 // One op over all chunks.  All pointers already validated.
@@ -228,16 +242,16 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk);
             LogitsParams lp{};
             lp.stats = stats; lp.E = G; lp.V = (int)pl.V; lp.V_pad = (int)pl.V_pad; lp.nst = (int)pl.nst;
-            lp.rows = (int)rc; lp.scale2 = scale2; lp.hdr = hdr;
+            lp.rows = (int)rc; lp.C = (int)pl.C; lp.scale2 = scale2; lp.hdr = hdr;
             lp.lse = lse_in ? lse_in + t0 : nullptr;
             lp.ignore = ignore ? ignore + t0 : nullptr;
             const dim3 grid = gemm_grid(g, 1);
             if (op == KD_OP_FORWARD)
-                launch_gemm<E, true, true, LogitsEpi<E, BM, BN, kStats>>(grid, stream, A, B, g, lp);
+                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kStats>>(grid, stream, A, B, g, lp);
             else if (op == KD_OP_FUSED)
-                launch_gemm<E, true, true, LogitsEpi<E, BM, BN, kFused>>(grid, stream, A, B, g, lp);
+                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kFused>>(grid, stream, A, B, g, lp);
             else
-                launch_gemm<E, true, true, LogitsEpi<E, BM, BN, kBwd>>(grid, stream, A, B, g, lp);
+                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kBwd>>(grid, stream, A, B, g, lp);
         }
         // ---- row kernel
         {
@@ -247,7 +261,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             rp.d = (int)pl.d; rp.V = (int)pl.V; rp.V_pad = (int)pl.V_pad; rp.K = (int)pl.K; rp.nst = (int)pl.nst;
             rp.inv_tau = 1.0f / pl.tau;
             rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.logit_bf16 = pl.logit_bf16; rp.ignore = ignore;
-            rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss;
+            rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss; rp.C = (int)pl.C;
             rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
             {
                 StageScope scope(KD_STAGE_ROWS, stream);
@@ -261,7 +275,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
         // ---- grad_H^T = W^T G^T (M = d, N = rc, K = V_pad)
         {
             const Operand A = operand(W, pl.d, pl.V * pl.d * es);
-            const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
+            const Operand B = g_operand(G, pl);
             const GemmGeom g = geom(pl.d, rc, pl.V_pad, pl.splits, bk);
             GradHParams hp{};
             hp.out = static_cast<char*>(grad_H) + t0 * pl.d * es;
@@ -269,7 +283,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             hp.direct = pl.splits == 1;
             {
                 StageScope scope(KD_STAGE_GRAD_H, stream);
-                launch_gemm<E, false, true, GradHEpi<E, BM, BN>>(gemm_grid(g, pl.splits), stream, A, B, g, hp);
+                launch_gemm<E, false, true, true, GradHEpi<E, BM, BN>>(gemm_grid(g, pl.splits), stream, A, B, g, hp);
             }
             if (pl.splits > 1) {
                 const int64_t n4 = rc * pl.d / 4;
@@ -282,11 +296,11 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
         {
             StageScope scope(KD_STAGE_GRAD_W, stream);
             const Operand A = operand(Hc, pl.d, rc * pl.d * es);
-            const Operand B = operand(G, pl.V_pad, rc * pl.V_pad * es);
+            const Operand B = g_operand(G, pl);
             const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 8);
             GradWParams wp{};
             wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0 || pl.accumulate;
-            launch_gemm<E, false, false, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp);
+            launch_gemm<E, false, false, true, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp);
         }
     }
     if (want_loss) hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, stream, hdr, loss);
