@@ -267,8 +267,10 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
     else:
-        # row kernel: reads and rewrites the chunk's G rows, reads partials
-        per_launch = rows_full * (2.0 * 2 * ((V + 255) // 256 * 256) + 8.0 * ((V + 255) // 256))
+        # row kernel: reads and rewrites the chunk's G rows, reads the (max, sum)
+        # partials (one per 128 ids) and the cached ids and logits
+        V_pad = (V + 255) // 256 * 256
+        per_launch = rows_full * (2.0 * 2 * V_pad + 8.0 * (V_pad // 128) + 8.0 * K)
         achieved = per_launch / (stages[dom]["avg_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
