@@ -26,7 +26,13 @@
 
 namespace kd {
 
-constexpr int kDtlThreads = 512;
+// Waves per workgroup: 8 (2 x 4, 128 x 64 per wave, two waves per SIMD) or 4
+// (2 x 2, 128 x 128 per wave, one wave per SIMD, accumulators in AGPRs).  On
+// the GPT-OSS-like step 4 waves measured 12-25% slower: with one wave per SIMD
+// nothing covers its LDS waits, load issue and barrier skew.
+constexpr int kDtlWaves = 8;
+static_assert(kDtlWaves == 8 || kDtlWaves == 4, "waves per workgroup");
+constexpr int kDtlThreads = 64 * kDtlWaves;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
@@ -83,21 +89,32 @@ __device__ __forceinline__ u32x2 lds_read8_tr(const lds_t* base, int off) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-// K step of the engine (bf16 elements).  An LDS stage holds the A and B tiles
-// of one step, 2 x 256 x 64 x 2 bytes = 64 KiB; two stages are in use.
+// K step of the engine (bf16 elements) and number of LDS stages.  A stage
+// holds the A and B tiles of one step, 2 x 256 x BK x 2 bytes.  K step 32 with
+// 4 or 5 stages (loads three or four steps ahead, spread evenly over the step)
+// measured 3-15% slower than 64 with 2: the per-step barrier and the 64-byte
+// row pieces of K-contiguous operands cost more than the deeper prefetch gains.
 constexpr int kDtlBK = 64;
-constexpr int kDtlTile = 256 * kDtlBK * 2;   // bytes of one operand tile per step
+constexpr int kDtlStages = 2;
+static_assert(kDtlBK == 32 || kDtlBK == 64, "K step");
+static_assert(kDtlStages >= 2 && kDtlStages * 2 * 256 * kDtlBK * 2 <= 160 * 1024, "stages fit the LDS");
+constexpr int kDtlSub = kDtlBK / 16;          // MFMA sub-steps (k = 16 each) per step
+constexpr int kDtlTile = 256 * kDtlBK * 2;    // bytes of one operand tile per step
 
-// K-contiguous tile of one step: [rows][64] bf16, 128-byte rows of eight
-// 16-byte chunks.  Chunk c of row r is stored at c ^ k_swz(r), chosen so that
-// a fragment read (32 consecutive rows, one chunk) touches distinct banks.
+// K-contiguous tile of one step: [rows][BK] bf16, rows of kCh 16-byte chunks.
+// Chunk c of row r is stored at c ^ k_swz(r), chosen so that a fragment read
+// (32 consecutive rows, one chunk) touches distinct banks in every group of 16
+// lanes (and of 8).
 constexpr int kRowBytes = kDtlBK * 2;
-__device__ __forceinline__ int k_swz(int r) { return (r ^ (r >> 3)) & 7; }
+constexpr int kCh = kDtlBK / 8;
+__device__ __forceinline__ int k_swz(int r) {
+    return kCh == 8 ? ((r ^ (r >> 3)) & 7) : (((r >> 1) ^ (r >> 3)) & 3);
+}
 __device__ __forceinline__ int k_off(int r, int c) {
     return r * kRowBytes + ((c ^ k_swz(r)) << 4);
 }
 
-// MN-contiguous tile of one step: [64][256] bf16, 512-byte k-rows of 32
+// MN-contiguous tile of one step: [BK][256] bf16, 512-byte k-rows of 32
 // chunks; chunk c of k-row k is stored at c ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 4).
 // A transposing read touches k-rows {k0..k0+3} (and k0+8.. in the other half
 // wave) x four consecutive chunks, which this places in distinct banks.
@@ -111,48 +128,40 @@ __device__ __forceinline__ int mn_off(int k, int m) {
 // step, instruction i of loader wave w filling LDS kilobyte w * NI + i of the
 // tile.  Instructions are issued one at a time between matrix instructions so
 // that a wave waiting for room in the texture-address queue delays at most one
-// MFMA of its own, while the other wave of the SIMD keeps the matrix core busy.
+// of its MFMAs.
 // ---------------------------------------------------------------------------
-#ifndef KD_STAGGER
-#define KD_STAGGER 0
-#endif
-#ifndef KD_LOADER_WAVES
-#if KD_STAGGER
-#define KD_LOADER_WAVES 8
-#else
-#define KD_LOADER_WAVES 4
-#endif
-#endif
-constexpr int kLoaderWaves = KD_LOADER_WAVES;
-static_assert(kLoaderWaves == 4 || kLoaderWaves == 8, "loader waves");
+constexpr int kLoaderWaves = 4;
 
 // BLOCKED operands are stored in blocks of 64 along one dimension with the
 // other dimension's rows 128 bytes apart inside a block (Operand::kblock bytes
-// from block to block): K-contiguous blocked = 64 k of every row per block (the
-// K step reads one block); MN-contiguous blocked = 64 m of every k per block.
+// from block to block): K-contiguous blocked = 64 k of every row per block;
+// MN-contiguous blocked = 64 m of every k per block.
 template <int ROWS, bool KMAJOR, bool BLOCKED = false> struct DtlLoader;
 
-// K-contiguous operand.  Load instruction i of loader wave w covers tile rows
-// 8 u .. 8 u + 7 (u = w NI + i); lane l reads logical chunk
-// (l & 7) ^ (l >> 3) ^ (u & 7) of row 8 u + (l >> 3), which lands in the
-// swizzled slot l & 7 of that row.
+// K-contiguous operand.  An instruction covers RPI = 1024 / kRowBytes rows;
+// instruction i of loader wave w covers tile rows RPI u .. RPI u + RPI - 1
+// (u = w NI + i); lane l writes slot l % kCh of row RPI u + l / kCh, so it
+// reads the logical chunk that the swizzle puts there.
 template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, true, BLOCKED> {
-    static_assert(ROWS == 256 && kRowBytes == 128, "tile rows and K step");
+    static_assert(ROWS == 256, "tile rows");
     static constexpr int NI = kDtlTile / 1024 / kLoaderWaves;
+    static constexpr int RPI = 1024 / kRowBytes;   // rows per instruction (8 or 16)
     Operand op;
-    uint64_t tile_off;   // byte offset of the tile's first row
+    uint64_t tile_off;   // byte offset of this wave's first row of the tile
     uint32_t lrow;       // byte offset of this lane's row within an instruction's rows
     int zl;              // lane part of the chunk index
 
     __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
         op = o;
-        tile_off = (uint64_t)m0 * (uint64_t)o.ld * 2u + (uint64_t)(wave * NI) * 16u * (uint64_t)o.ld;
-        lrow = (uint32_t)(2 * (lane >> 3) * o.ld);
-        zl = (lane & 7) ^ (lane >> 3) ^ ((wave * NI) & 7);
+        tile_off = (uint64_t)m0 * (uint64_t)o.ld * 2u + (uint64_t)(wave * NI * RPI) * 2u * (uint64_t)o.ld;
+        lrow = (uint32_t)(2 * (lane / kCh) * o.ld);
+        // k_swz of row RPI u + l / kCh without the part that depends on u
+        if constexpr (kCh == 8) zl = (lane & 7) ^ (lane >> 3) ^ ((wave * NI) & 7);
+        else zl = (lane & 3) ^ ((lane >> 3) & 3) ^ (lane >> 5);
     }
     __device__ __forceinline__ u32x4 rsrc(int k0) const {
-        // blocked: ld = 64 and the step's 64 k are block k0 / 64
-        if constexpr (BLOCKED) return window_rsrc(op, tile_off + (uint64_t)(k0 >> 6) * op.kblock);
+        // blocked: ld = 64 and k0 lies in block k0 / 64
+        if constexpr (BLOCKED) return window_rsrc(op, tile_off + (uint64_t)(k0 >> 6) * op.kblock + (uint64_t)(k0 & 63) * 2u);
         else return window_rsrc(op, tile_off + (uint64_t)k0 * 2u);
     }
     __device__ __forceinline__ void hide() {
@@ -162,26 +171,36 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, true, BLOCKED> {
     // instruction i of the step at k0 into the tile at LDS byte address `tile`
     __device__ __forceinline__ void issue1(const u32x4& rs, uint32_t tile, int i, int k0, int kend, bool full,
                                            int wave) const {
-        const int c = zl ^ i;
-        uint32_t v = lrow + (uint32_t)(i * 16 * op.ld) + (uint32_t)(c << 4);
+        int c;
+        if constexpr (kCh == 8) c = zl ^ i;
+        else c = zl ^ (2 * ((wave * NI + i) & 1));
+        uint32_t v = lrow + (uint32_t)(i * RPI * 2 * op.ld) + (uint32_t)(c << 4);
         if (!full && k0 + c * 8 >= kend) v = kOOB;
         dtl_load16(rs, tile + (uint32_t)((wave * NI + i) * 1024), v);
     }
-    // Fragment addresses: 32-row fragment f (rows base + 32 f ..) of sub-step s
-    // (k = 16 s ..) is at off[s ^ 2 (f & 1)] + 4096 f for this lane.
+    // Fragment addresses: 32-row fragment f (rows base + 32 f ..) of sub-step
+    // s (k = 16 s ..) is at off[s ^ 2 (f & 1)] + 4096 f (K step 64) or
+    // off[s] + 2048 f (K step 32) for this lane.
     struct Frag {
-        int off[4];
+        int off[kDtlSub];
     };
     static __device__ __forceinline__ Frag frag_addr(int base, int lane) {
-        const int x = (lane >> 5) ^ (lane & 7) ^ ((lane >> 3) & 3);
         const int rowb = (base + (lane & 31)) * kRowBytes;
         Frag f;
+        if constexpr (kCh == 8) {
+            const int x = (lane >> 5) ^ (lane & 7) ^ ((lane >> 3) & 3);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) f.off[y] = rowb + ((x ^ (2 * y)) << 4);
+            for (int y = 0; y < 4; ++y) f.off[y] = rowb + ((x ^ (2 * y)) << 4);
+        } else {
+            const int x = (lane >> 5) ^ (((lane >> 1) ^ (lane >> 3)) & 3);
+#pragma unroll
+            for (int y = 0; y < 2; ++y) f.off[y] = rowb + ((x ^ (2 * y)) << 4);
+        }
         return f;
     }
     static __device__ __forceinline__ u32x4 frag(const lds_t* tile, const Frag& fa, int f, int s) {
-        return lds_read16(tile, fa.off[s ^ (2 * (f & 1))] + 4096 * f);
+        if constexpr (kCh == 8) return lds_read16(tile, fa.off[s ^ (2 * (f & 1))] + 4096 * f);
+        else return lds_read16(tile, fa.off[s] + 2048 * f);
     }
 };
 
@@ -247,16 +266,18 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, false, BLOCKED> {
     }
 };
 
-// Accumulators of one wave: (BM/2) x (BN/4) as 32 x 32 fragments.
+// Accumulators of one wave: (BM/2) x (BN/WN) as 32 x 32 fragments, the
+// waves laid out 2 (M) x WN (N).
 template <int BM, int BN> struct DtlMma {
-    static constexpr int FM = BM / 64;   // 4
-    static constexpr int FN = BN / 128;  // 2
+    static constexpr int WN = kDtlWaves / 2;
+    static constexpr int FM = BM / 64;          // 4
+    static constexpr int FN = BN / WN / 32;     // 2 (8 waves) or 4 (4 waves)
     f32x16 acc[FM][FN];
     static __device__ __forceinline__ int row(int wm, int i, int q, int lane) {
         return wm * (BM / 2) + 32 * i + 8 * q + 4 * (lane >> 5);
     }
     static __device__ __forceinline__ int col(int wn, int j, int lane) {
-        return wn * (BN / 4) + 32 * j + (lane & 31);
+        return wn * (BN / WN) + 32 * j + (lane & 31);
     }
 };
 
@@ -269,46 +290,55 @@ __device__ __forceinline__ void wave_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// LDS of the engine: two pipeline stages of kDtlStage bytes (A tile, then B tile).
+// LDS of the engine: kDtlStages pipeline stages of kDtlStage bytes (A tile,
+// then B tile).
 constexpr int kDtlStage = 2 * kDtlTile;
-constexpr int kDtlLds = 2 * kDtlStage;
+constexpr int kDtlLds = kDtlStages * kDtlStage;
+static_assert(kDtlLds >= 128 * 1024, "the epilogues stage through 128 KiB of LDS");
+
+// s_waitcnt immediate (gfx9): vmcnt (6 bits, split), expcnt 7, lgkmcnt.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
 
 // ---------------------------------------------------------------------------
-// Main loop.  Per K step a wave runs four sub-steps of eight MFMAs; the
+// Main loop.  Per K step a wave runs kDtlSub sub-steps of FM x FN MFMAs; the
 // operand fragments of sub-step s + 1 are read from LDS while the MFMAs of
 // sub-step s run (two register sets), and the last sub-step's MFMAs run after
 // the barrier that publishes the next stage, so they cover the latency of the
-// next stage's first fragment reads.  The loads of step it + 1 are issued in
-// the first two MFMA groups after that barrier, into the stage every wave has
-// just finished reading, and are awaited at the end of step it.
+// next stage's first fragment reads.
+//
+// Stages form a ring: step j lives in stage j mod NS.  The stage of step it is
+// free once every wave has passed the barrier that ends step it's reads, so
+// the loads of step j are issued partly on the MFMA group after the barrier
+// that frees its stage (kPost instructions per loader wave) and the rest on
+// the groups of the following step before its barrier; they have NS - 2
+// further steps to land before the barrier that publishes step j.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool B_BLOCKED, class Epi>
 __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B, const GemmGeom& g,
                                               const typename Epi::Params& ep, lds_t* smem) {
     static_assert(BM == 256 && BN == 256, "tile shape");
-    constexpr int BK = kDtlBK;
+    constexpr int BK = kDtlBK, NS = kDtlStages, SUB = kDtlSub;
     using LA = DtlLoader<BM, A_KMAJOR>;
     using LB = DtlLoader<BN, B_KMAJOR, B_BLOCKED>;
     using Mma = DtlMma<BM, BN>;
-    constexpr int FM = Mma::FM, FN = Mma::FN;
+    constexpr int FM = Mma::FM, FN = Mma::FN, WN = Mma::WN;
     constexpr int NT = LA::NI + LB::NI;          // load instructions per step and loader wave
-    // S0 of them ride on the MFMA group that follows each barrier (for the
-    // step two ahead, the earliest a stage is free), the other S1 on the next
-    // group (for the step after the current one).  Issuing everything as
-    // early as possible measured best: two loads after each of the eight
-    // MFMAs of that group.  kBurst issues a group's share ahead of its MFMAs.
-#ifdef KD_DMA_S0
-    constexpr int S0 = KD_DMA_S0;
-#else
-    constexpr int S0 = NT;
-#endif
-#ifdef KD_DMA_BURST
-    constexpr bool kBurst = KD_DMA_BURST;
-#else
-    constexpr bool kBurst = false;
-#endif
-    constexpr int S1 = NT - S0;
-    static_assert(S0 >= 0 && S1 >= 0, "load shares");
+    // two stages: every load rides on the group right after the barrier (the
+    // earliest its stage is free; measured best); more stages: half and half
+    constexpr int kPost = NS == 2 ? NT : NT / 2;
+    static_assert(kPost >= 0 && kPost <= NT, "load shares");
+    constexpr int kPre = NT - kPost;             // spread over the SUB - 1 groups before the barrier
+    // loads issued after the last one of step it + 1 when the barrier ending
+    // step it is reached in the steady state
+    constexpr int kAhead = (NS - 2) * NT;
+    static_assert(kAhead + kPost <= 63, "vmcnt range");
 
     int tm, tn;
     if (!tile_of(g, tm, tn)) return;
@@ -321,7 +351,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WN, wn = wave % WN;
     const bool loader = wave < kLoaderWaves;
 
     LA la;
@@ -339,10 +369,11 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
             for (int e = 0; e < 16; ++e) mma.acc[i][j][e] = 0.f;
 
     typename LA::Frag fa = LA::frag_addr(wm * (BM / 2), lane);
-    typename LB::Frag fb = LB::frag_addr(wn * (BN / 4), lane);
+    typename LB::Frag fb = LB::frag_addr(wn * (BN / WN), lane);
     struct Frags {
         u32x4 a[FM], b[FN];
     };
+    auto stage = [&](int step) { return smem + (int)((unsigned)step % (unsigned)NS) * kDtlStage; };
     // FMV: fragments of this wave's rows that hold output rows below M (the
     // others are neither read nor multiplied)
     auto read = [&](Frags& f, const lds_t* tile, int s, auto fmv_c) {
@@ -359,20 +390,20 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         mma.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
                                                                __builtin_bit_cast(bf16x8, f.b[j]), mma.acc[i][j], 0, 0, 0);
     };
-    // loads of one step, in flight between two barriers
+    // the loads of one step
     struct Pending {
         u32x4 ra, rb;
         uint32_t tile;
         int k0;
         bool full;
     };
-    auto pending_for = [&](int step, const lds_t* tile) {
+    auto pending_for = [&](int step) {
         Pending p;
         p.k0 = kbeg + step * BK;
         p.full = p.k0 + BK <= kend;
         p.ra = la.rsrc(p.k0);
         p.rb = lb.rsrc(p.k0);
-        p.tile = lds_addr_of(tile);
+        p.tile = lds_addr_of(stage(step));
         return p;
     };
     auto load1 = [&](const Pending& p, int q) {
@@ -384,12 +415,9 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         constexpr int first = decltype(first_c)::value, CNT = decltype(cnt_c)::value;
         constexpr int NQ = decltype(fmv_c)::value * FN;
         if constexpr (decltype(with_loads)::value && CNT > 0) {
-            if constexpr (kBurst || NQ == 0) {
+            if constexpr (NQ == 0) {
 #pragma unroll
                 for (int t = 0; t < CNT; ++t) load1(p, first + t);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) mfma1(f, q);
             } else {
                 // load t follows MFMA (t * NQ) / CNT
 #pragma unroll
@@ -410,66 +438,81 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     };
     using Z = std::integral_constant<int, 0>;
 
-    // Main loop of one wave whose loads ride as S0c instructions on the group
-    // after each barrier (for the step two ahead) and S1c on the group after
-    // that (for the next step).
-    auto run = [&](auto S0c, auto S1c, auto FMVc) {
-        constexpr int s0 = decltype(S0c)::value, s1 = decltype(S1c)::value;
-        static_assert(s0 + s1 == 0 || s0 + s1 == NT, "a loader wave issues all its instructions");
-        using C0 = std::integral_constant<int, s0>;
-        using C1 = std::integral_constant<int, s1>;
+    // Main loop of one wave; LOADS: this wave issues loads.
+    auto run = [&](auto LOADS, auto FMVc) {
+        constexpr bool loads = decltype(LOADS)::value;
         Frags f0, f1;
-        if constexpr (s0 + s1 > 0) {
-            // step 0, and the share of step 1 that would have ridden on step -1
-            const Pending p = pending_for(0, smem);
+        if constexpr (loads) {
+            // steps 0 .. NS - 2, and the share of step NS - 1 that would have
+            // ridden on the group after the barrier before step 0
 #pragma unroll
-            for (int q = 0; q < NT; ++q) load1(p, q);
-            if (nk > 1) {
-                const Pending p1 = pending_for(1, smem + kDtlStage);
+            for (int j = 0; j + 1 < NS; ++j) {
+                if (j < nk) {
+                    const Pending p = pending_for(j);
 #pragma unroll
-                for (int q = 0; q < s0; ++q) load1(p1, q);
-                __builtin_amdgcn_s_waitcnt(0x0F70 | s0);   // vmcnt(s0): step 0 landed
+                    for (int q = 0; q < NT; ++q) load1(p, q);
+                }
+            }
+            if (NS - 1 < nk) {
+                const Pending p = pending_for(NS - 1);
+#pragma unroll
+                for (int q = 0; q < kPost; ++q) load1(p, q);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kAhead + kPost, 15));   // step 0 landed
             } else {
-                __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
             }
         }
         wave_barrier();
         read(f0, smem, 0, FMVc);
-        // One K step.  LD1 / LD0: this step carries the loads of step it + 1 /
-        // it + 2 (compile-time, so the MFMA groups stay free of branches).
-        auto body = [&](auto LD1, auto LD0, int it) {
+        // One K step.  PRE / POST: the groups before / after this step's
+        // barrier carry loads of step it + NS - 1 / it + NS (compile-time, so
+        // the MFMA groups stay free of branches).
+        auto body = [&](auto PRE, auto POST, int it) {
             la.hide();
             lb.hide();
 #pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                opaque(fa.off[y]);
-                opaque(fb.off[y]);
-            }
-            lds_t* cur = smem + (it & 1) * kDtlStage;
-            lds_t* nxt = smem + ((it + 1) & 1) * kDtlStage;
-            Pending p1{}, p0{};
-            if constexpr (decltype(LD1)::value && s1 > 0) p1 = pending_for(it + 1, nxt);   // free since the last barrier
-            read(f1, cur, 1, FMVc);
-            group(f0, LD1, p1, C0{}, C1{}, FMVc);
-            read(f0, cur, 2, FMVc);
-            group(f1, std::false_type{}, p1, Z{}, Z{}, FMVc);
-            read(f1, cur, 3, FMVc);
-            group(f0, std::false_type{}, p1, Z{}, Z{}, FMVc);
+            for (int y = 0; y < (int)(sizeof(fa.off) / sizeof(int)); ++y) opaque(fa.off[y]);
+#pragma unroll
+            for (int y = 0; y < (int)(sizeof(fb.off) / sizeof(int)); ++y) opaque(fb.off[y]);
+            constexpr bool pre = decltype(PRE)::value && loads && kPre > 0;
+            constexpr bool post = decltype(POST)::value && loads && kPost > 0;
+            const lds_t* cur = stage(it);
+            Pending pp{}, pq{};
+            if constexpr (pre) pp = pending_for(it + NS - 1);   // its stage is free since the last barrier
+            // sub-steps 0 .. SUB - 2: read the next sub-step's fragments, then
+            // the MFMAs of this one with a share of the loads
+            static_for<SUB - 1>([&](auto S) {
+                constexpr int s = decltype(S)::value;
+                constexpr int lo = kPost + (s * kPre) / (SUB - 1);
+                constexpr int hi = kPost + ((s + 1) * kPre) / (SUB - 1);
+                using First = std::integral_constant<int, lo>;
+                using Cnt = std::integral_constant<int, hi - lo>;
+                if constexpr (s % 2 == 0) {
+                    read(f1, cur, s + 1, FMVc);
+                    group(f0, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc);
+                } else {
+                    read(f0, cur, s + 1, FMVc);
+                    group(f1, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc);
+                }
+            });
+            static_assert(SUB % 2 == 0, "the last sub-step uses the second register set");
             if (it + 1 < nk) {
                 // this wave's loads of step it + 1 and its reads of `cur` are complete
-                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+                if constexpr (decltype(PRE)::value) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kAhead, 0));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
                 wave_barrier();                       // every wave's loads landed; `cur` is free
-                read(f0, nxt, 0, FMVc);
+                read(f0, stage(it + 1), 0, FMVc);
             }
-            if constexpr (decltype(LD0)::value && s0 > 0) p0 = pending_for(it + 2, cur);
-            group(f1, LD0, p0, Z{}, C0{}, FMVc);           // sub-step 3
+            if constexpr (post) pq = pending_for(it + NS);
+            // sub-step SUB - 1
+            group(f1, std::integral_constant<bool, post>{}, pq, Z{}, std::integral_constant<int, kPost>{}, FMVc);
         };
         const std::true_type yes{};
         const std::false_type no{};
         int it = 0;
-        for (; it + 2 < nk; ++it) body(yes, yes, it);
-        if (it + 1 < nk) body(yes, no, it++);
-        body(no, no, it);
+        for (; it + NS < nk; ++it) body(yes, yes, it);
+        if (it + NS - 1 < nk) body(yes, no, it++);
+        for (; it < nk; ++it) body(no, no, it);
     };
     if (nk > 0) {
         // rows of this wave's half below M: all (4 fragments), at most 64 (2)
@@ -479,20 +522,13 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         const int fmv = rem > 64 ? 4 : (rem > 0 ? 2 : 0);
         using F4 = std::integral_constant<int, 4>;
         using F2 = std::integral_constant<int, 2>;
-        auto dispatch = [&](auto S0c, auto S1c) {
-            if (fmv == 4)      run(S0c, S1c, F4{});
-            else if (fmv == 2) run(S0c, S1c, F2{});
-            else               run(S0c, S1c, Z{});
+        auto dispatch = [&](auto LOADS) {
+            if (fmv == 4)      run(LOADS, F4{});
+            else if (fmv == 2) run(LOADS, F2{});
+            else               run(LOADS, Z{});
         };
-#if KD_STAGGER
-        // every wave loads; the two waves of a SIMD take turns (wm = 0 right
-        // after the barrier, wm = 1 one group later)
-        if (wm == 0) dispatch(std::integral_constant<int, NT>{}, Z{});
-        else         dispatch(Z{}, std::integral_constant<int, NT>{});
-#else
-        if (loader) dispatch(std::integral_constant<int, S0>{}, std::integral_constant<int, S1>{});
-        else        dispatch(Z{}, Z{});
-#endif
+        if (loader) dispatch(std::true_type{});
+        else        dispatch(std::false_type{});
     }
     __syncthreads();   // LDS is reused by epilogues
     Epi::apply(mma, m0, n0, split, wm, wn, lane, tid, smem, ep);

@@ -87,9 +87,10 @@ __device__ __forceinline__ void stage_flush(const lds_t* st, uint16_t* dst, int6
     const int wave = tid >> 6, lane = tid & 63;
     const int c = lane & 31;
     const int64_t blk = (int64_t)(v0 / kGBlock + (c >> 3)) * C;
+    constexpr int RW = 256 / kDtlWaves;   // staged rows per wave
 #pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
-        const int tl = wave * 32 + 2 * k + (lane >> 5);
+    for (int k = 0; k < RW / 2; ++k) {
+        const int tl = wave * RW + 2 * k + (lane >> 5);
         const u32x4 val = lds_read16(st, stage_off(tl, c));
         const int t = n0 + tl;
         if (t < rows) *reinterpret_cast<u32x4*>(dst + (blk + t) * kGBlock + (c & 7) * 8) = val;
@@ -304,9 +305,10 @@ template <typename E, int BM, int BN> struct GradWEpi {
                 __syncthreads();
                 const int c = lane & 31;
                 const int h = m0 + 128 * half + 4 * c;
+                constexpr int RW = 256 / kDtlWaves;   // staged rows per wave
 #pragma unroll 8
-                for (int k = 0; k < 16; ++k) {
-                    const int vl = wave * 32 + 2 * k + (lane >> 5);
+                for (int k = 0; k < RW / 2; ++k) {
+                    const int vl = wave * RW + 2 * k + (lane >> 5);
                     f32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
                         smem + vl * 512 + ((c ^ (vl & 31)) << 4));
                     const int v = n0 + vl;
