@@ -113,24 +113,30 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
         }
     }
 
+    // The accumulators hold raw logits z; base-2 values are y = z * scale2
+    // (scale2 = log2(e) / tau > 0), formed inside the exponent with one fma.
+    // Ids at or beyond V (the padding of the last vocabulary tile only) are
+    // excluded as -inf.
     template <class Mma>
     static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int /*split*/, int wm, int wn,
                                                  int lane, int tid, lds_t* smem, const Params& p) {
         constexpr int FM = Mma::FM, FN = Mma::FN;
-        // base-2 logits; ids at or beyond V are excluded (-inf)
+        const float sc = p.scale2;
+        if (m0 + BM > p.V) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int v0 = m0 + Mma::row(wm, i, q, lane);
+                for (int q = 0; q < 4; ++q) {
+                    const int v0 = m0 + Mma::row(wm, i, q, lane);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool ok = v0 + r < p.V;
+                    for (int r = 0; r < 4; ++r) {
+                        const bool ok = v0 + r < p.V;
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        mma.acc[i][j][4 * q + r] = ok ? mma.acc[i][j][4 * q + r] * p.scale2 : -INFINITY;
+                        for (int j = 0; j < FN; ++j)
+                            mma.acc[i][j][4 * q + r] = ok ? mma.acc[i][j][4 * q + r] : -INFINITY;
+                    }
                 }
-            }
+        }
 
         if constexpr (MODE == kBwd) {
             const float s = p.hdr->s;
@@ -147,7 +153,7 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                     for (int q = 0; q < 4; ++q) {
                         float g[4];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) g[r] = st * fast_exp2(mma.acc[i][j][4 * q + r] - l2);
+                        for (int r = 0; r < 4; ++r) g[r] = st * fast_exp2(fmaf(mma.acc[i][j][4 * q + r], sc, -l2));
                         if constexpr (kStaged)
                             stage_write4<Mma>(smem, wm, wn, i, j, q, lane, g[0], g[1], g[2], g[3]);
                         else if (live)
@@ -161,29 +167,32 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
             return;
         } else {
             // this wave's 128 ids of each of its columns (lanes l and l + 32
-            // hold the same column): max, then exp2 relative to it and the sum
+            // hold the same column): max, then exp2 relative to it and the sum.
+            // scale2 > 0, so the max of y is the scaled max of z.
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                float mx = -INFINITY;
+                float mz = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, mma.acc[i][j][e]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-                const bool none = mx == -INFINITY;   // every id of the block is beyond V
+                    for (int e = 0; e < 16; ++e) mz = fmaxf(mz, mma.acc[i][j][e]);
+                mz = fmaxf(mz, __shfl_xor(mz, 32, kWave));
+                const float my = mz * sc;
+                // every id of the block beyond V: all terms are exp2(-inf) = 0
+                const float off = mz == -INFINITY ? 0.f : my;
                 float sum = 0.f;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const float x = none ? 0.f : fast_exp2(mma.acc[i][j][e] - mx);
+                        const float x = fast_exp2(fmaf(mma.acc[i][j][e], sc, -off));
                         mma.acc[i][j][e] = x;
                         sum += x;
                     }
                 sum += __shfl_xor(sum, 32, kWave);
                 const int t = n0 + Mma::col(wn, j, lane);
                 if (lane < 32 && t < p.rows)
-                    p.stats[(int64_t)t * p.nst + (m0 / BM) * 2 + wm] = f32x2{mx, sum};
+                    p.stats[(int64_t)t * p.nst + (m0 / BM) * 2 + wm] = f32x2{my, sum};
             }
             if constexpr (MODE == kFused) {
                 if constexpr (kStaged) {
