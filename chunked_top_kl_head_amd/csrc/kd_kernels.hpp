@@ -424,6 +424,7 @@ struct RowParams {
     float* row_loss;        // [T] or null
     float* chunk_loss;      // [C]
     void* G;                // C x V_pad, GLayout<E>
+    int2* sparse;           // kFused: [C][K] (id or -1, G value bits) of the cached entries
     const WsHeader* hdr;
 };
 
@@ -489,7 +490,6 @@ __device__ __forceinline__ float dot_row_bf16_unrolled(const void* h, const void
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
-    extern __shared__ float dyn[];           // nst floats (kFused rescale factors)
     __shared__ float sh_p[kMaxK], sh_lp[kMaxK], sh_a[kMaxK];
     __shared__ int sh_id[kMaxK];
     __shared__ float red[4];
@@ -517,12 +517,6 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
         lse2 = p.lse_in[t] * kLog2e;
     }
 
-    // 16-byte chunk c of this row of G (16 / sizeof(E) ids, never across a block)
-    constexpr int kEpc = 16 / Elem<E>::size;
-    auto gchunk = [&](int c) {
-        return reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.G) +
-                                        GLayout<E>::index(r, (int64_t)c * kEpc, p.C, p.V_pad) * Elem<E>::size);
-    };
     if (!kept) {
         if (p.mode != kBwd) {
             if (tid == 0) {
@@ -531,8 +525,10 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
             }
         }
         if (p.mode == kFused) {
-            const int nch = p.V_pad / kEpc;
-            for (int c = tid; c < nch; c += kThreads) *gchunk(c) = u32x4{0u, 0u, 0u, 0u};
+            // factor 0 makes rescale_kernel write zeros; no cached entries
+            float* fac = reinterpret_cast<float*>(const_cast<f32x2*>(p.stats + (int64_t)r * p.nst));
+            for (int i = tid; i < p.nst; i += kThreads) fac[2 * i] = 0.f;
+            for (int k = tid; k < p.K; k += kThreads) p.sparse[(int64_t)r * p.K + k] = int2{-1, 0};
         }
         return;
     }
@@ -591,65 +587,125 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     }
 
     const float s = p.hdr->s;
-    // 5. kFused: e * 2^(tile max - lse2) * s  ->  dense part of G
+    // 5. kFused: the factor s * 2^(block max - lse2) that turns the stored
+    // e = 2^(y - block max) of each 128-id block into the dense part of G
+    // replaces the block's max in the stats (rescale_kernel applies it)
     if (p.mode == kFused) {
-        const f32x2* st = p.stats + (int64_t)r * p.nst;
-        for (int i = tid; i < p.nst; i += kThreads) dyn[i] = s * fast_exp2(st[i][0] - lse2);
-        __syncthreads();
-        if constexpr (Elem<E>::size == 2) {
-            // U chunks per thread in flight: the row is a pure stream
-            const int nch = p.V_pad / 8;
-            constexpr int U = 8;
-            auto scale = [&](u32x4& v, int c) {
-                const float f = dyn[c >> 4];   // 16 chunks per 128-id block
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[q] = pack_bf16x2(bf16_bits_to_f32(v[q] & 0xFFFFu) * f, bf16_bits_to_f32(v[q] >> 16) * f);
-            };
-            int c = tid;
-            for (; c + (U - 1) * kThreads < nch; c += U * kThreads) {
-                u32x4 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = *gchunk(c + u * kThreads);
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    scale(v[u], c + u * kThreads);
-                    *gchunk(c + u * kThreads) = v[u];
-                }
-            }
-            for (; c < nch; c += kThreads) {
-                u32x4 v = *gchunk(c);
-                scale(v, c);
-                *gchunk(c) = v;
-            }
-        } else {
-            const int nch = p.V_pad / 4;
-            for (int c = tid; c < nch; c += kThreads) {
-                const float f = dyn[(c * 4) / kStatIds];
-                f32x4* g = reinterpret_cast<f32x4*>(gchunk(c));
-                *g = *g * f;
-            }
-        }
-        __syncthreads();
+        f32x2* st = const_cast<f32x2*>(p.stats + (int64_t)r * p.nst);
+        float* fac = reinterpret_cast<float*>(st);
+        for (int i = tid; i < p.nst; i += kThreads) fac[2 * i] = s * fast_exp2(st[i][0] - lse2);
     }
 
-    // 6. cached entries: G = s (q - P), P summing duplicate ids; first occurrence writes
+    // 6. cached entries: G = s (q - P), P summing duplicate ids; first occurrence
+    // writes (kFused: into the sparse list, written into G after the rescale)
     for (int k = tid; k < K; k += kThreads) {
         const int id = sh_id[k];
         bool first = true;
         for (int k2 = 0; k2 < k; ++k2) first &= (sh_id[k2] != id);
-        if (!first) continue;
+        if (!first) {
+            if (p.mode == kFused) p.sparse[(int64_t)r * K + k] = int2{-1, 0};
+            continue;
+        }
         float P = sh_p[k];
         for (int k2 = k + 1; k2 < K; ++k2) P += (sh_id[k2] == id) ? sh_p[k2] : 0.f;
         const float q = fast_exp2(sh_a[k] * kLog2e - lse2);
         const float gval = s * (q - P);
-        if constexpr (Elem<E>::size == 2) {
+        if (p.mode == kFused) {
+            p.sparse[(int64_t)r * K + k] = int2{id, __float_as_int(gval)};
+        } else if constexpr (Elem<E>::size == 2) {
             reinterpret_cast<uint16_t*>(p.G)[GLayout<E>::index(r, id, p.C, p.V_pad)] =
                 (uint16_t)(pack_bf16x2(gval, 0.f) & 0xFFFFu);
         } else {
             reinterpret_cast<float*>(p.G)[GLayout<E>::index(r, id, p.C, p.V_pad)] = gval;
         }
     }
+}
+
+// kFused: G = factor(row, 128-id block) * e over the chunk's G buffer in its
+// physical order, rows < rows only; factor 0 (an ignored row) writes zeros.
+// Each workgroup streams kRescaleSpan contiguous 16-byte chunks: bf16 (blocked
+// layout) grid = (C * 8 / span, V_pad / 64), one 64-id block per grid row;
+// fp32 (row-major) grid = (C, V_pad / 4 / span), one row per grid column.
+constexpr int kRescaleU = 8;                          // chunks in flight per thread
+constexpr int kRescaleSpan = kThreads * kRescaleU;    // chunks per workgroup
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void rescale_kernel(void* G, const f32x2* fac, int nst, int C, int V_pad,
+                                                           int rows) {
+    constexpr int kEpc = 16 / Elem<E>::size;          // elements per 16-byte chunk
+    int64_t base;                                     // first chunk of this workgroup
+    int64_t end;                                      // end of its contiguous range
+    int r0, v0;                                       // (row, id) of chunk `base`
+    if constexpr (GLayout<E>::kBlocked) {
+        const int per_blk = C * (kGBlock / kEpc);     // chunks of one 64-id block
+        const int w0 = (int)blockIdx.x * kRescaleSpan;
+        base = (int64_t)blockIdx.y * per_blk + w0;
+        end = (int64_t)blockIdx.y * per_blk + min(per_blk, w0 + kRescaleSpan);
+        r0 = w0 / (kGBlock / kEpc);
+        v0 = (int)blockIdx.y * kGBlock;
+    } else {
+        const int per_row = V_pad / kEpc;
+        const int w0 = (int)blockIdx.y * kRescaleSpan;
+        base = (int64_t)blockIdx.x * per_row + w0;
+        end = (int64_t)blockIdx.x * per_row + min(per_row, w0 + kRescaleSpan);
+        r0 = (int)blockIdx.x;
+        v0 = w0 * kEpc;
+    }
+    // chunk base + w -> (row, id)
+    auto where = [&](int w, int& r, int& v) {
+        if constexpr (GLayout<E>::kBlocked) {
+            r = r0 + w / (kGBlock / kEpc);
+            v = v0 + (w % (kGBlock / kEpc)) * kEpc;
+        } else {
+            r = r0;
+            v = v0 + w * kEpc;
+        }
+    };
+    auto scale = [&](u32x4& x, float f) {
+        if constexpr (Elem<E>::size == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                x[q] = f == 0.f ? 0u : pack_bf16x2(bf16_bits_to_f32(x[q] & 0xFFFFu) * f, bf16_bits_to_f32(x[q] >> 16) * f);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = f == 0.f ? 0u : __float_as_uint(__uint_as_float(x[q]) * f);
+        }
+    };
+    u32x4* g = reinterpret_cast<u32x4*>(G);
+    u32x4 x[kRescaleU];
+    float f[kRescaleU];
+    bool live[kRescaleU];
+#pragma unroll
+    for (int u = 0; u < kRescaleU; ++u) {
+        const int w = u * kThreads + (int)threadIdx.x;
+        int r, v;
+        where(w, r, v);
+        live[u] = base + w < end && r < rows;
+        f[u] = live[u] ? fac[(int64_t)r * nst + v / kStatIds][0] : 0.f;
+        x[u] = live[u] ? g[base + w] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kRescaleU; ++u) {
+        if (!live[u]) continue;
+        scale(x[u], f[u]);
+        g[base + u * kThreads + (int)threadIdx.x] = x[u];
+    }
+}
+
+// kFused: the cached entries of the sparse list into G (after the rescale).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void sparse_kernel(void* G, const int2* sparse, int64_t n, int K, int C,
+                                                          int V_pad) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const int2 e = sparse[i];
+    if (e.x < 0) return;
+    const int64_t at = GLayout<E>::index(i / K, e.x, C, V_pad);
+    const float gval = __int_as_float(e.y);
+    if constexpr (Elem<E>::size == 2)
+        reinterpret_cast<uint16_t*>(G)[at] = (uint16_t)(pack_bf16x2(gval, 0.f) & 0xFFFFu);
+    else
+        reinterpret_cast<float*>(G)[at] = gval;
 }
 
 // Sum of the chunk's row losses in a fixed order, added to the running total.

@@ -69,7 +69,7 @@ struct Plan {
     int splits;           // grad_H splits over the vocabulary
     bool accumulate;      // grad_W += instead of =
     bool logit_bf16;      // teacher logits are bf16
-    size_t off_hdr, off_closs, off_stats, off_G, off_part, total;
+    size_t off_hdr, off_closs, off_stats, off_G, off_part, off_sparse, total;
 };
 
 // Optional event tables of the profiling hook (kd_topk_kl_set_stage_events).
@@ -166,6 +166,8 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
     if (op != KD_OP_FORWARD) o = align256(o + (size_t)(q.C * q.V_pad * q.es));
     q.off_part = o;
     if (op != KD_OP_FORWARD && q.splits > 1) o = align256(o + sizeof(float) * (size_t)(q.splits * q.C * q.d));
+    q.off_sparse = o;
+    if (op == KD_OP_FUSED) o = align256(o + sizeof(int2) * (size_t)(q.C * q.K));
     q.total = o;
     *pl = q;
     return KD_OK;
@@ -263,10 +265,24 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.logit_bf16 = pl.logit_bf16; rp.ignore = ignore;
             rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss; rp.C = (int)pl.C;
             rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
+            rp.sparse = reinterpret_cast<int2*>(wsb + pl.off_sparse);
             {
                 StageScope scope(KD_STAGE_ROWS, stream);
-                hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), (size_t)(pl.nst * sizeof(float)),
-                                   stream, rp);
+                hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), 0, stream, rp);
+                if (op == KD_OP_FUSED) {
+                    // dense part of G: the stored exponentials times the row kernel's
+                    // per-block factors, streamed in the buffer's own order; then the
+                    // cached entries
+                    const int epc = 16 / es;
+                    const dim3 rg = es == 2 ? dim3((unsigned)cdiv(pl.C * (kGBlock / epc), (int64_t)kRescaleSpan),
+                                                   (unsigned)(pl.V_pad / kGBlock))
+                                            : dim3((unsigned)pl.C, (unsigned)cdiv(pl.V_pad / epc, (int64_t)kRescaleSpan));
+                    hipLaunchKernelGGL(rescale_kernel<E>, rg, dim3(kThreads), 0, stream, G, stats, (int)pl.nst,
+                                       (int)pl.C, (int)pl.V_pad, (int)rc);
+                    const int64_t n = rc * pl.K;
+                    hipLaunchKernelGGL(sparse_kernel<E>, dim3((unsigned)cdiv(n, (int64_t)kThreads)), dim3(kThreads), 0,
+                                       stream, G, rp.sparse, n, (int)pl.K, (int)pl.C, (int)pl.V_pad);
+                }
             }
             if (want_loss)
                 hipLaunchKernelGGL(loss_chunk_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, closs, (int)rc);
