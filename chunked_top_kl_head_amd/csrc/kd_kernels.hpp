@@ -293,8 +293,25 @@ template <typename E, int BM, int BN> struct GradWEpi {
             // (16-byte chunk c of row v at c ^ (v & 31)), then every wave
             // updates whole 512-byte row segments of grad_W.
             const int wave = tid >> 6;
+            const int c = lane & 31;
+            constexpr int RW = 256 / kDtlWaves;   // staged rows per wave
+            constexpr int NK = RW / 2;            // 16-byte pieces per thread and half
+            // this thread's pieces of grad_W: the first half's are read before
+            // anything is staged, the second half's as the first half's stores
+            // free their registers, so the latency overlaps staging and barriers
+            auto load_old = [&](int half, int k) {
+                const int v = n0 + wave * RW + 2 * k + (lane >> 5);
+                const int h = m0 + 128 * half + 4 * c;
+                return (p.accumulate && v < p.V && h < p.d)
+                           ? *reinterpret_cast<const f32x4*>(p.gw + (int64_t)v * p.d + h)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+            };
+            f32x4 old[NK];
+#pragma unroll
+            for (int k = 0; k < NK; ++k) old[k] = load_old(0, k);
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
+                const int h = m0 + 128 * half + 4 * c;
                 if (wm == half) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
@@ -303,29 +320,24 @@ template <typename E, int BM, int BN> struct GradWEpi {
                         for (int i = 0; i < FM; ++i)
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
-                                const int h = Mma::row(0, i, q, lane);   // within the half, multiple of 4
+                                const int hh = Mma::row(0, i, q, lane);   // within the half, multiple of 4
                                 const f32x4 val = {mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1],
                                                    mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]};
                                 *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(
-                                    smem + v * 512 + (((h >> 2) ^ (v & 31)) << 4)) = val;
+                                    smem + v * 512 + (((hh >> 2) ^ (v & 31)) << 4)) = val;
                             }
                     }
                 }
                 __syncthreads();
-                const int c = lane & 31;
-                const int h = m0 + 128 * half + 4 * c;
-                constexpr int RW = 256 / kDtlWaves;   // staged rows per wave
-#pragma unroll 8
-                for (int k = 0; k < RW / 2; ++k) {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
                     const int vl = wave * RW + 2 * k + (lane >> 5);
-                    f32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                    const f32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
                         smem + vl * 512 + ((c ^ (vl & 31)) << 4));
                     const int v = n0 + vl;
-                    if (v < p.V && h < p.d) {
-                        f32x4* dst = reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h);
-                        if (p.accumulate) val += *dst;
-                        *dst = val;
-                    }
+                    if (v < p.V && h < p.d)
+                        *reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h) = val + old[k];
+                    if (half == 0) old[k] = load_old(1, k);
                 }
                 if (half == 0) __syncthreads();
             }
