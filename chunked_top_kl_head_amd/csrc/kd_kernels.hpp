@@ -476,28 +476,50 @@ __device__ __forceinline__ float dot_row(const E* h, const E* w, int d, int lane
     return wave_sum(acc);
 }
 
-// bf16 dot product of two rows of d = 8 nc elements with every load of a row
-// issued before the first multiply (NR >= ceil(nc / 64) chunks per lane).
+// The wave's share of the K dot products H_t . W_id (bf16 rows of nc 16-byte
+// chunks, NR >= ceil(nc / 64) chunks per lane): the H row stays in registers,
+// and NP W rows are loaded before any of them is multiplied (NP = 2 measured
+// best: 3 and 4 lose more to occupancy than they gain).  Writes z / tau.
 template <int NR>
-__device__ __forceinline__ float dot_row_bf16_unrolled(const void* h, const void* w, int nc, int lane) {
+__device__ __forceinline__ void dots_bf16(const void* h, const void* W, const int* ids, int K, int d, int nc,
+                                          int wave, int lane, float inv_tau, float* out) {
+    constexpr int NW = kThreads / kWave;
+    constexpr int NP = 2;
     const u32x4* hv = reinterpret_cast<const u32x4*>(h);
-    const u32x4* wv = reinterpret_cast<const u32x4*>(w);
-    u32x4 a[NR], b[NR];
+    u32x4 a[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int c = lane + kWave * r;
         a[r] = c < nc ? hv[c] : u32x4{0u, 0u, 0u, 0u};
-        b[r] = c < nc ? wv[c] : u32x4{0u, 0u, 0u, 0u};
     }
-    float acc = 0.f;
+    for (int k = wave; k < K; k += NP * NW) {
+        u32x4 b[NP][NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+        for (int j = 0; j < NP; ++j) {
+            const int kk = k + j * NW;
+            const u32x4* w = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) +
+                                                            (int64_t)ids[kk < K ? kk : k] * d);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc = fmaf(bf16_bits_to_f32(a[r][q] & 0xFFFFu), bf16_bits_to_f32(b[r][q] & 0xFFFFu), acc);
-            acc = fmaf(bf16_bits_to_f32(a[r][q] >> 16), bf16_bits_to_f32(b[r][q] >> 16), acc);
+            for (int r = 0; r < NR; ++r) {
+                const int c = lane + kWave * r;
+                b[j][r] = (c < nc && kk < K) ? w[c] : u32x4{0u, 0u, 0u, 0u};
+            }
         }
-    return wave_sum(acc);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc = fmaf(bf16_bits_to_f32(a[r][q] & 0xFFFFu), bf16_bits_to_f32(b[j][r][q] & 0xFFFFu), acc);
+                    acc = fmaf(bf16_bits_to_f32(a[r][q] >> 16), bf16_bits_to_f32(b[j][r][q] >> 16), acc);
+                }
+            const float z = wave_sum(acc);
+            const int kk = k + j * NW;
+            if (lane == 0 && kk < K) out[kk] = z * inv_tau;
+        }
+    }
 }
 
 template <typename E>
@@ -569,18 +591,20 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     const int wave = tid >> 6, lane = tid & 63;
     const E* hrow = reinterpret_cast<const E*>(p.H) + (int64_t)t * p.d;
     const int nc8 = p.d / 8;   // 16-byte chunks of a bf16 row
-    for (int k = wave; k < K; k += kThreads / kWave) {
-        const E* wrow = reinterpret_cast<const E*>(p.W) + (int64_t)sh_id[k] * p.d;
-        float z;
-        if constexpr (Elem<E>::size == 2) {
-            if (nc8 <= 2 * kWave)      z = dot_row_bf16_unrolled<2>(hrow, wrow, nc8, lane);
-            else if (nc8 <= 4 * kWave) z = dot_row_bf16_unrolled<4>(hrow, wrow, nc8, lane);
-            else if (nc8 <= 6 * kWave) z = dot_row_bf16_unrolled<6>(hrow, wrow, nc8, lane);
-            else                       z = dot_row<E>(hrow, wrow, p.d, lane);
-        } else {
-            z = dot_row<E>(hrow, wrow, p.d, lane);
+    bool done = false;
+    if constexpr (Elem<E>::size == 2) {
+        done = true;
+        if (nc8 <= 2 * kWave)      dots_bf16<2>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
+        else if (nc8 <= 4 * kWave) dots_bf16<4>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
+        else if (nc8 <= 6 * kWave) dots_bf16<6>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
+        else                       done = false;
+    }
+    if (!done) {
+        for (int k = wave; k < K; k += kThreads / kWave) {
+            const E* wrow = reinterpret_cast<const E*>(p.W) + (int64_t)sh_id[k] * p.d;
+            const float z = dot_row<E>(hrow, wrow, p.d, lane);
+            if (lane == 0) sh_a[k] = z * p.inv_tau;
         }
-        if (lane == 0) sh_a[k] = z * p.inv_tau;
     }
     __syncthreads();
     const float lse = lse2 * kLn2;
