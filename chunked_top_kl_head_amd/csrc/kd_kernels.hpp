@@ -24,7 +24,8 @@ struct WsHeader {
     double loss_acc;   // running sum of row losses (fixed chunk order)
     int64_t N;         // number of kept positions
     float s;           // g / (tau N), 0 when N = 0
-    float pad[11];
+    int dirty;         // fused entry: rows of the current chunk that need rescaling
+    float pad[10];
 };
 static_assert(sizeof(WsHeader) <= 256, "header slot");
 
@@ -62,7 +63,13 @@ struct LogitsParams {
     const float* lse;      // kBwd: natural-log lse of the chunk rows
     const uint8_t* ignore; // kBwd: ignore flags of the chunk rows (may be null)
     const WsHeader* hdr;   // kBwd: s
+    const float* ref;      // kStats / kFused: per-row base-2 reference R0 (of the sums and stored exponentials)
 };
+
+// kFused: a block whose max exceeds the row's reference R0 by more than this
+// (base 2) stores its exponentials relative to its own max instead, so every
+// stored value is at most 2^kRefSlack and no row can overflow.
+constexpr float kRefSlack = 64.f;
 
 // bf16 logit tiles leave through LDS so that every global store writes whole
 // 512-byte rows: the MFMA layout gives a lane four consecutive vocabulary ids
@@ -167,8 +174,12 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
             return;
         } else {
             // this wave's 128 ids of each of its columns (lanes l and l + 32
-            // hold the same column): max, then exp2 relative to it and the sum.
-            // scale2 > 0, so the max of y is the scaled max of z.
+            // hold the same column): max, then exp2 relative to a reference and
+            // the sum.  scale2 > 0, so the max of y is the scaled max of z.
+            // The reference is the row's R0 (the largest student logit at its
+            // cached ids), unless the block max exceeds it by more than
+            // kRefSlack -- then the block max; the forward and fused entries
+            // thus produce identical statistics.
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 float mz = -INFINITY;
@@ -177,9 +188,15 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) mz = fmaxf(mz, mma.acc[i][j][e]);
                 mz = fmaxf(mz, __shfl_xor(mz, 32, kWave));
-                const float my = mz * sc;
-                // every id of the block beyond V: all terms are exp2(-inf) = 0
-                const float off = mz == -INFINITY ? 0.f : my;
+                const int t = n0 + Mma::col(wn, j, lane);
+                float my = mz * sc;
+                {
+                    const float r0 = t < p.rows ? p.ref[t] : -INFINITY;
+                    my = my <= r0 + kRefSlack ? r0 : my;
+                }
+                // every id of the block beyond V (kStats) or no reference: all
+                // terms are exp2(-inf) = 0
+                const float off = my == -INFINITY ? 0.f : my;
                 float sum = 0.f;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
@@ -190,7 +207,6 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                         sum += x;
                     }
                 sum += __shfl_xor(sum, 32, kWave);
-                const int t = n0 + Mma::col(wn, j, lane);
                 if (lane < 32 && t < p.rows)
                     p.stats[(int64_t)t * p.nst + (m0 / BM) * 2 + wm] = f32x2{my, sum};
             }
@@ -231,9 +247,10 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
 // fixed-order reduction sums.
 // ---------------------------------------------------------------------------
 struct GradHParams {
-    void* out;        // grad_H of the chunk's first row (element type)
-    float* partial;   // [splits][C][d] fp32
+    void* out;            // grad_H of the chunk's first row (element type)
+    float* partial;       // [splits][C][d] fp32
     int d, rows, C, direct;
+    const float* fscale;  // fused entry: per-row factor of G (G = fscale_t * stored values), else null
 };
 
 template <typename E, int BM, int BN> struct GradHEpi {
@@ -246,14 +263,15 @@ template <typename E, int BM, int BN> struct GradHEpi {
         for (int j = 0; j < FN; ++j) {
             const int t = n0 + Mma::col(wn, j, lane);
             if (t >= p.rows) continue;
+            const float f = p.fscale ? p.fscale[t] : 1.f;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int h = m0 + Mma::row(wm, i, q, lane);
                     if (h >= p.d) continue;
-                    const f32x4 v = {mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
-                                     mma.acc[i][j][4 * q + 3]};
+                    const f32x4 v = {mma.acc[i][j][4 * q] * f, mma.acc[i][j][4 * q + 1] * f,
+                                     mma.acc[i][j][4 * q + 2] * f, mma.acc[i][j][4 * q + 3] * f};
                     if (p.direct) {
                         if constexpr (Elem<E>::size == 2) {
                             u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -416,8 +434,19 @@ __global__ __launch_bounds__(kThreads) void prepass_kernel(WsHeader* hdr, const 
 //   distribution comes from the cached top-K logits),
 //   student logits at the cached ids as K dot products H_t . W_id,
 //   row loss  L = sum_k p_k (log p_k - a_k + lse),
-//   kFused: rescale the row's exp2(y - tile max) into G = s (q - P) in place,
-//   kFused/kBwd: replace the K cached entries by s (q - P).
+//   kBwd: replace the K cached entries of G by s (q - P).
+// The forward and fused entries run it twice per chunk.  Before the logits
+// GEMM (pre): the dot products, kept for later, and the row's reference
+// R0 = max_k y_k (base 2), relative to which the GEMM sums (and, fused,
+// stores) the exponentials.  After it: lse, loss and, fused, the factor that
+// turns the stored exponentials into G.  The GEMM stores 2^(y - R0) wherever a block's max stays within
+// kRefSlack of R0 (the usual case: some cached id is among the student's
+// largest logits), so G = s 2^(R0 - lse) * stored value with one factor per
+// row, which the gradient GEMMs apply (grad_H in its epilogue, grad_W through
+// a scaled copy of the chunk's H).  A row with a block stored relative to its
+// own max R_b is marked dirty: every block is brought to the row's largest
+// reference by rescale_kernel.  The cached entries are stored as
+// 2^(y_k - R) - P_k 2^(lse - R), i.e. s (q - P) divided by the row factor.
 // ---------------------------------------------------------------------------
 struct RowParams {
     int mode;
@@ -436,8 +465,14 @@ struct RowParams {
     float* row_loss;        // [T] or null
     float* chunk_loss;      // [C]
     void* G;                // C x V_pad, GLayout<E>
-    int2* sparse;           // kFused: [C][K] (id or -1, G value bits) of the cached entries
-    const WsHeader* hdr;
+    int2* sparse;           // kFused: [C][K] (id or -1, stored value bits) of the cached entries
+    WsHeader* hdr;
+    // fused entry
+    int pre;                // 1: the pass before the logits GEMM (dot products and references)
+    float* zc;              // [C][K] student logits a = z / tau at the cached ids
+    float* ref;             // [C] base-2 reference R0 of the stored exponentials
+    float* fscale;          // [C] G = fscale_t * stored values
+    uint8_t* dirty;         // [C] 1: some block of the row is stored relative to its own max
 };
 
 constexpr int kMaxK = 1024;
@@ -531,9 +566,55 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     const int t = p.t0 + r;
     const int tid = (int)threadIdx.x;
     const bool kept = (p.ignore == nullptr) || (p.ignore[t] == 0);
+    const int K = p.K;
+    const int wave = tid >> 6, lane = tid & 63;
+    const bool fused = p.mode == kFused;
+    const bool two_pass = p.mode != kBwd;   // forward and fused entries: a pass before the logits GEMM
 
-    // 1. lse of the row
-    float lse2;
+    // student logits at the cached ids (the split backward; the forward and
+    // fused entries compute them in their first pass)
+    auto dots = [&]() {
+        const E* hrow = reinterpret_cast<const E*>(p.H) + (int64_t)t * p.d;
+        const int nc8 = p.d / 8;   // 16-byte chunks of a bf16 row
+        bool done = false;
+        if constexpr (Elem<E>::size == 2) {
+            done = true;
+            if (nc8 <= 2 * kWave)      dots_bf16<2>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
+            else if (nc8 <= 4 * kWave) dots_bf16<4>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
+            else if (nc8 <= 6 * kWave) dots_bf16<6>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
+            else                       done = false;
+        }
+        if (!done) {
+            for (int k = wave; k < K; k += kThreads / kWave) {
+                const E* wrow = reinterpret_cast<const E*>(p.W) + (int64_t)sh_id[k] * p.d;
+                const float z = dot_row<E>(hrow, wrow, p.d, lane);
+                if (lane == 0) sh_a[k] = z * p.inv_tau;
+            }
+        }
+        __syncthreads();
+    };
+
+    if (two_pass && p.pre) {
+        if (r == 0 && tid == 0) p.hdr->dirty = 0;
+        if (!kept) {
+            if (tid == 0) p.ref[r] = 0.f;   // any finite reference: the row's G is multiplied by 0
+            return;
+        }
+        for (int k = tid; k < K; k += kThreads) sh_id[k] = clamp_id(p.idx[(int64_t)t * K + k], p.V);
+        __syncthreads();
+        dots();
+        float ym = -INFINITY;
+        for (int k = tid; k < K; k += kThreads) {
+            p.zc[(int64_t)r * K + k] = sh_a[k];
+            ym = fmaxf(ym, sh_a[k] * kLog2e);
+        }
+        ym = block_max(ym, red);
+        if (tid == 0) p.ref[r] = ym;
+        return;
+    }
+
+    // 1. lse of the row; Mall = the largest block reference
+    float lse2, Mall = 0.f;
     if (p.mode != kBwd) {
         const f32x2* st = p.stats + (int64_t)r * p.nst;
         float M = -INFINITY, S = 0.f;
@@ -543,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
             if (Mn > -INFINITY) S = S * fast_exp2(M - Mn) + v[1] * fast_exp2(v[0] - Mn);
             M = Mn;
         }
-        const float Mall = block_max(M, red);
+        Mall = block_max(M, red);
         const float Sall = block_sum(M > -INFINITY ? S * fast_exp2(M - Mall) : 0.f, red);
         lse2 = Mall + fast_log2(Sall);
         if (tid == 0 && p.lse_out) p.lse_out[t] = lse2 * kLn2;
@@ -558,22 +639,24 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
                 if (p.row_loss) p.row_loss[t] = 0.f;
             }
         }
-        if (p.mode == kFused) {
-            // factor 0 makes rescale_kernel write zeros; no cached entries
-            float* fac = reinterpret_cast<float*>(const_cast<f32x2*>(p.stats + (int64_t)r * p.nst));
-            for (int i = tid; i < p.nst; i += kThreads) fac[2 * i] = 0.f;
-            for (int k = tid; k < p.K; k += kThreads) p.sparse[(int64_t)r * p.K + k] = int2{-1, 0};
+        if (fused) {
+            // factor 0: the row contributes nothing; no cached entries
+            if (tid == 0) {
+                p.fscale[r] = 0.f;
+                p.dirty[r] = 0;
+            }
+            for (int k = tid; k < K; k += kThreads) p.sparse[(int64_t)r * K + k] = int2{-1, 0};
         }
         return;
     }
 
     // 2. teacher distribution over the cached entries
-    const int K = p.K;
     float bmax = -INFINITY;
     for (int k = tid; k < K; k += kThreads) {
         const float b = teacher_logit(p.logit, p.logit_bf16, (int64_t)t * K + k) * p.inv_tau;
         sh_lp[k] = b;
         sh_id[k] = clamp_id(p.idx[(int64_t)t * K + k], p.V);
+        if (two_pass) sh_a[k] = p.zc[(int64_t)r * K + k];
         bmax = fmaxf(bmax, b);
     }
     bmax = block_max(bmax, red);
@@ -588,25 +671,8 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     }
 
     // 3. student logits at the cached ids
-    const int wave = tid >> 6, lane = tid & 63;
-    const E* hrow = reinterpret_cast<const E*>(p.H) + (int64_t)t * p.d;
-    const int nc8 = p.d / 8;   // 16-byte chunks of a bf16 row
-    bool done = false;
-    if constexpr (Elem<E>::size == 2) {
-        done = true;
-        if (nc8 <= 2 * kWave)      dots_bf16<2>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
-        else if (nc8 <= 4 * kWave) dots_bf16<4>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
-        else if (nc8 <= 6 * kWave) dots_bf16<6>(hrow, p.W, sh_id, K, p.d, nc8, wave, lane, p.inv_tau, sh_a);
-        else                       done = false;
-    }
-    if (!done) {
-        for (int k = wave; k < K; k += kThreads / kWave) {
-            const E* wrow = reinterpret_cast<const E*>(p.W) + (int64_t)sh_id[k] * p.d;
-            const float z = dot_row<E>(hrow, wrow, p.d, lane);
-            if (lane == 0) sh_a[k] = z * p.inv_tau;
-        }
-    }
-    __syncthreads();
+    if (!two_pass) dots();
+    else __syncthreads();
     const float lse = lse2 * kLn2;
 
     // 4. row loss (entries with p = 0 contribute 0)
@@ -623,32 +689,44 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     }
 
     const float s = p.hdr->s;
-    // 5. kFused: the factor s * 2^(block max - lse2) that turns the stored
-    // e = 2^(y - block max) of each 128-id block into the dense part of G
-    // replaces the block's max in the stats (rescale_kernel applies it)
-    if (p.mode == kFused) {
-        f32x2* st = const_cast<f32x2*>(p.stats + (int64_t)r * p.nst);
-        float* fac = reinterpret_cast<float*>(st);
-        for (int i = tid; i < p.nst; i += kThreads) fac[2 * i] = s * fast_exp2(st[i][0] - lse2);
+    // 5. fused: the row factor and, for a dirty row, the per-block factors
+    // 2^(R_b - Mall) (each <= 1) in place of the blocks' references
+    if (fused) {
+        const bool clean = Mall == p.ref[r];
+        if (tid == 0) {
+            p.fscale[r] = s * fast_exp2(Mall - lse2);
+            p.dirty[r] = clean ? 0 : 1;
+            if (!clean) atomicAdd(&p.hdr->dirty, 1);
+        }
+        if (!clean) {
+            f32x2* st = const_cast<f32x2*>(p.stats + (int64_t)r * p.nst);
+            float* fac = reinterpret_cast<float*>(st);
+            for (int i = tid; i < p.nst; i += kThreads) fac[2 * i] = fast_exp2(st[i][0] - Mall);
+        }
     }
 
     // 6. cached entries: G = s (q - P), P summing duplicate ids; first occurrence
-    // writes (kFused: into the sparse list, written into G after the rescale)
+    // writes (fused: into the sparse list as s (q - P) / row factor, written
+    // into G after any rescale)
+    const float up = fast_exp2(lse2 - Mall);
     for (int k = tid; k < K; k += kThreads) {
         const int id = sh_id[k];
         bool first = true;
         for (int k2 = 0; k2 < k; ++k2) first &= (sh_id[k2] != id);
         if (!first) {
-            if (p.mode == kFused) p.sparse[(int64_t)r * K + k] = int2{-1, 0};
+            if (fused) p.sparse[(int64_t)r * K + k] = int2{-1, 0};
             continue;
         }
         float P = sh_p[k];
         for (int k2 = k + 1; k2 < K; ++k2) P += (sh_id[k2] == id) ? sh_p[k2] : 0.f;
+        if (fused) {
+            const float val = fast_exp2(sh_a[k] * kLog2e - Mall) - P * up;
+            p.sparse[(int64_t)r * K + k] = int2{id, __float_as_int(val)};
+            continue;
+        }
         const float q = fast_exp2(sh_a[k] * kLog2e - lse2);
         const float gval = s * (q - P);
-        if (p.mode == kFused) {
-            p.sparse[(int64_t)r * K + k] = int2{id, __float_as_int(gval)};
-        } else if constexpr (Elem<E>::size == 2) {
+        if constexpr (Elem<E>::size == 2) {
             reinterpret_cast<uint16_t*>(p.G)[GLayout<E>::index(r, id, p.C, p.V_pad)] =
                 (uint16_t)(pack_bf16x2(gval, 0.f) & 0xFFFFu);
         } else {
@@ -657,17 +735,20 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     }
 }
 
-// kFused: G = factor(row, 128-id block) * e over the chunk's G buffer in its
-// physical order, rows < rows only; factor 0 (an ignored row) writes zeros.
-// Each workgroup streams kRescaleSpan contiguous 16-byte chunks: bf16 (blocked
-// layout) grid = (C * 8 / span, V_pad / 64), one 64-id block per grid row;
-// fp32 (row-major) grid = (C, V_pad / 4 / span), one row per grid column.
+// Fused entry, dirty rows only: stored value *= 2^(R_b - Mall) per 128-id
+// block (the factors the row kernel left in the block statistics), in place,
+// over the chunk's G buffer in its physical order.  Each workgroup streams
+// kRescaleSpan contiguous 16-byte chunks: bf16 (blocked layout) grid =
+// (C * 8 / span, V_pad / 64), one 64-id block per grid row; fp32 (row-major)
+// grid = (C, V_pad / 4 / span), one row per grid column.  When no row of the
+// chunk is dirty every workgroup exits at once.
 constexpr int kRescaleU = 8;                          // chunks in flight per thread
 constexpr int kRescaleSpan = kThreads * kRescaleU;    // chunks per workgroup
 
 template <typename E>
-__global__ __launch_bounds__(kThreads) void rescale_kernel(void* G, const f32x2* fac, int nst, int C, int V_pad,
-                                                           int rows) {
+__global__ __launch_bounds__(kThreads) void rescale_kernel(void* G, const f32x2* fac, const uint8_t* dirty,
+                                                           const WsHeader* hdr, int nst, int C, int V_pad, int rows) {
+    if (hdr->dirty == 0) return;
     constexpr int kEpc = 16 / Elem<E>::size;          // elements per 16-byte chunk
     int64_t base;                                     // first chunk of this workgroup
     int64_t end;                                      // end of its contiguous range
@@ -701,10 +782,10 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(void* G, const f32x2*
         if constexpr (Elem<E>::size == 2) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                x[q] = f == 0.f ? 0u : pack_bf16x2(bf16_bits_to_f32(x[q] & 0xFFFFu) * f, bf16_bits_to_f32(x[q] >> 16) * f);
+                x[q] = pack_bf16x2(bf16_bits_to_f32(x[q] & 0xFFFFu) * f, bf16_bits_to_f32(x[q] >> 16) * f);
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) x[q] = f == 0.f ? 0u : __float_as_uint(__uint_as_float(x[q]) * f);
+            for (int q = 0; q < 4; ++q) x[q] = __float_as_uint(__uint_as_float(x[q]) * f);
         }
     };
     u32x4* g = reinterpret_cast<u32x4*>(G);
@@ -716,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(void* G, const f32x2*
         const int w = u * kThreads + (int)threadIdx.x;
         int r, v;
         where(w, r, v);
-        live[u] = base + w < end && r < rows;
+        live[u] = base + w < end && r < rows && dirty[r] != 0;
         f[u] = live[u] ? fac[(int64_t)r * nst + v / kStatIds][0] : 0.f;
         x[u] = live[u] ? g[base + w] : u32x4{0u, 0u, 0u, 0u};
     }
@@ -742,6 +823,28 @@ __global__ __launch_bounds__(kThreads) void sparse_kernel(void* G, const int2* s
         reinterpret_cast<uint16_t*>(G)[at] = (uint16_t)(pack_bf16x2(gval, 0.f) & 0xFFFFu);
     else
         reinterpret_cast<float*>(G)[at] = gval;
+}
+
+// Fused entry: Hs = fscale_t * H_t for the chunk's rows (rounded to the element
+// type), the grad_W operand that carries G's per-row factor.  Grid: rows x
+// ceil(d / 8 / 256) workgroups of 16-byte chunks (8 bf16 or 4 fp32 elements).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void scale_rows_kernel(const void* H, void* Hs, const float* fscale, int d) {
+    constexpr int kEpc = 16 / Elem<E>::size;
+    const int r = (int)blockIdx.y;
+    const int c = (int)blockIdx.x * kThreads + (int)threadIdx.x;
+    if (c * kEpc >= d) return;
+    const float f = fscale[r];
+    u32x4 x = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(H) + (int64_t)r * d * Elem<E>::size)[c];
+    if constexpr (Elem<E>::size == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            x[q] = pack_bf16x2(bf16_bits_to_f32(x[q] & 0xFFFFu) * f, bf16_bits_to_f32(x[q] >> 16) * f);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = __float_as_uint(__uint_as_float(x[q]) * f);
+    }
+    reinterpret_cast<u32x4*>(reinterpret_cast<char*>(Hs) + (int64_t)r * d * Elem<E>::size)[c] = x;
 }
 
 // Sum of the chunk's row losses in a fixed order, added to the running total.

@@ -69,7 +69,7 @@ struct Plan {
     int splits;           // grad_H splits over the vocabulary
     bool accumulate;      // grad_W += instead of =
     bool logit_bf16;      // teacher logits are bf16
-    size_t off_hdr, off_closs, off_stats, off_G, off_part, off_sparse, total;
+    size_t off_hdr, off_closs, off_stats, off_G, off_part, off_sparse, off_zc, off_ref, off_fscale, off_dirty, off_Hs, total;
 };
 
 // Optional event tables of the profiling hook (kd_topk_kl_set_stage_events).
@@ -168,6 +168,19 @@ static kd_status make_plan(const kd_problem* p, kd_op op, Plan* pl) {
     if (op != KD_OP_FORWARD && q.splits > 1) o = align256(o + sizeof(float) * (size_t)(q.splits * q.C * q.d));
     q.off_sparse = o;
     if (op == KD_OP_FUSED) o = align256(o + sizeof(int2) * (size_t)(q.C * q.K));
+    // forward and fused entries: cached-id logits and row references; fused:
+    // row factors, dirty flags and the row-scaled copy of the chunk's H (the
+    // grad_W operand)
+    q.off_zc = o;
+    if (op != KD_OP_BACKWARD) o = align256(o + sizeof(float) * (size_t)(q.C * q.K));
+    q.off_ref = o;
+    if (op != KD_OP_BACKWARD) o = align256(o + sizeof(float) * (size_t)q.C);
+    q.off_fscale = o;
+    if (op == KD_OP_FUSED) o = align256(o + sizeof(float) * (size_t)q.C);
+    q.off_dirty = o;
+    if (op == KD_OP_FUSED) o = align256(o + (size_t)q.C);
+    q.off_Hs = o;
+    if (op == KD_OP_FUSED) o = align256(o + (size_t)(q.C * q.d * q.es));
     q.total = o;
     *pl = q;
     return KD_OK;
@@ -223,6 +236,12 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
     f32x2* stats = reinterpret_cast<f32x2*>(wsb + pl.off_stats);
     void* G = wsb + pl.off_G;
     float* part = reinterpret_cast<float*>(wsb + pl.off_part);
+    float* zc = reinterpret_cast<float*>(wsb + pl.off_zc);
+    float* ref = reinterpret_cast<float*>(wsb + pl.off_ref);
+    float* fscale = reinterpret_cast<float*>(wsb + pl.off_fscale);
+    uint8_t* dirty = reinterpret_cast<uint8_t*>(wsb + pl.off_dirty);
+    void* Hs = wsb + pl.off_Hs;
+    const bool fused = op == KD_OP_FUSED;
     const int es = pl.es, bk = 128 / es;
     const bool want_grads = op != KD_OP_FORWARD;
     const bool want_loss = op != KD_OP_BACKWARD;
@@ -236,6 +255,23 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
     for (int64_t t0 = 0; t0 < pl.T; t0 += pl.C) {
         const int64_t rc = pl.T - t0 < pl.C ? pl.T - t0 : pl.C;
         const char* Hc = static_cast<const char*>(H) + t0 * pl.d * es;
+        RowParams rp{};
+        rp.mode = op == KD_OP_FORWARD ? kStats : (fused ? kFused : kBwd);
+        rp.t0 = (int)t0; rp.rows = (int)rc;
+        rp.d = (int)pl.d; rp.V = (int)pl.V; rp.V_pad = (int)pl.V_pad; rp.K = (int)pl.K; rp.nst = (int)pl.nst;
+        rp.inv_tau = 1.0f / pl.tau;
+        rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.logit_bf16 = pl.logit_bf16; rp.ignore = ignore;
+        rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss; rp.C = (int)pl.C;
+        rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
+        rp.sparse = reinterpret_cast<int2*>(wsb + pl.off_sparse);
+        rp.zc = zc; rp.ref = ref; rp.fscale = fscale; rp.dirty = dirty;
+        if (op != KD_OP_BACKWARD) {
+            // ---- dot products at the cached ids and the rows' references
+            StageScope scope(KD_STAGE_ROWS, stream);
+            rp.pre = 1;
+            hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), 0, stream, rp);
+            rp.pre = 0;
+        }
         // ---- logits GEMM: Z^T = W H_c^T (M = V_pad, N = rc, K = d)
         {
             StageScope scope(KD_STAGE_LOGITS, stream);
@@ -247,46 +283,39 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             lp.rows = (int)rc; lp.C = (int)pl.C; lp.scale2 = scale2; lp.hdr = hdr;
             lp.lse = lse_in ? lse_in + t0 : nullptr;
             lp.ignore = ignore ? ignore + t0 : nullptr;
+            lp.ref = ref;
             const dim3 grid = gemm_grid(g, 1);
             if (op == KD_OP_FORWARD)
                 launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kStats>>(grid, stream, A, B, g, lp);
-            else if (op == KD_OP_FUSED)
+            else if (fused)
                 launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kFused>>(grid, stream, A, B, g, lp);
             else
                 launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kBwd>>(grid, stream, A, B, g, lp);
         }
         // ---- row kernel
         {
-            RowParams rp{};
-            rp.mode = op == KD_OP_FORWARD ? kStats : (op == KD_OP_FUSED ? kFused : kBwd);
-            rp.t0 = (int)t0; rp.rows = (int)rc;
-            rp.d = (int)pl.d; rp.V = (int)pl.V; rp.V_pad = (int)pl.V_pad; rp.K = (int)pl.K; rp.nst = (int)pl.nst;
-            rp.inv_tau = 1.0f / pl.tau;
-            rp.H = H; rp.W = W; rp.idx = idx; rp.logit = logit; rp.logit_bf16 = pl.logit_bf16; rp.ignore = ignore;
-            rp.stats = stats; rp.lse_in = lse_in; rp.lse_out = lse_out; rp.row_loss = row_loss; rp.C = (int)pl.C;
-            rp.chunk_loss = closs; rp.G = G; rp.hdr = hdr;
-            rp.sparse = reinterpret_cast<int2*>(wsb + pl.off_sparse);
-            {
-                StageScope scope(KD_STAGE_ROWS, stream);
-                hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), 0, stream, rp);
-                if (op == KD_OP_FUSED) {
-                    // dense part of G: the stored exponentials times the row kernel's
-                    // per-block factors, streamed in the buffer's own order; then the
-                    // cached entries
-                    const int epc = 16 / es;
-                    const dim3 rg = es == 2 ? dim3((unsigned)cdiv(pl.C * (kGBlock / epc), (int64_t)kRescaleSpan),
-                                                   (unsigned)(pl.V_pad / kGBlock))
-                                            : dim3((unsigned)pl.C, (unsigned)cdiv(pl.V_pad / epc, (int64_t)kRescaleSpan));
-                    hipLaunchKernelGGL(rescale_kernel<E>, rg, dim3(kThreads), 0, stream, G, stats, (int)pl.nst,
-                                       (int)pl.C, (int)pl.V_pad, (int)rc);
-                    const int64_t n = rc * pl.K;
-                    hipLaunchKernelGGL(sparse_kernel<E>, dim3((unsigned)cdiv(n, (int64_t)kThreads)), dim3(kThreads), 0,
-                                       stream, G, rp.sparse, n, (int)pl.K, (int)pl.C, (int)pl.V_pad);
-                }
+            StageScope scope(KD_STAGE_ROWS, stream);
+            hipLaunchKernelGGL(row_kernel<E>, dim3((unsigned)rc), dim3(kThreads), 0, stream, rp);
+            if (fused) {
+                // dirty rows only: every block brought to the row's largest
+                // reference; then the cached entries; then the row-scaled H_c
+                const int epc = 16 / es;
+                const dim3 rg = es == 2 ? dim3((unsigned)cdiv(pl.C * (kGBlock / epc), (int64_t)kRescaleSpan),
+                                               (unsigned)(pl.V_pad / kGBlock))
+                                        : dim3((unsigned)pl.C, (unsigned)cdiv(pl.V_pad / epc, (int64_t)kRescaleSpan));
+                hipLaunchKernelGGL(rescale_kernel<E>, rg, dim3(kThreads), 0, stream, G, stats, dirty, hdr,
+                                   (int)pl.nst, (int)pl.C, (int)pl.V_pad, (int)rc);
+                const int64_t n = rc * pl.K;
+                hipLaunchKernelGGL(sparse_kernel<E>, dim3((unsigned)cdiv(n, (int64_t)kThreads)), dim3(kThreads), 0,
+                                   stream, G, rp.sparse, n, (int)pl.K, (int)pl.C, (int)pl.V_pad);
+                if (want_grads)
+                    hipLaunchKernelGGL(scale_rows_kernel<E>, dim3((unsigned)cdiv(pl.d / epc, (int64_t)kThreads),
+                                                                  (unsigned)rc),
+                                       dim3(kThreads), 0, stream, Hc, Hs, fscale, (int)pl.d);
             }
-            if (want_loss)
-                hipLaunchKernelGGL(loss_chunk_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, closs, (int)rc);
         }
+        if (want_loss)
+            hipLaunchKernelGGL(loss_chunk_kernel, dim3(1), dim3(kThreads), 0, stream, hdr, closs, (int)rc);
         if (!want_grads) continue;
         // ---- grad_H^T = W^T G^T (M = d, N = rc, K = V_pad)
         {
@@ -297,6 +326,7 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             hp.out = static_cast<char*>(grad_H) + t0 * pl.d * es;
             hp.partial = part; hp.d = (int)pl.d; hp.rows = (int)rc; hp.C = (int)pl.C;
             hp.direct = pl.splits == 1;
+            hp.fscale = fused ? fscale : nullptr;
             {
                 StageScope scope(KD_STAGE_GRAD_H, stream);
                 launch_gemm<E, false, true, true, GradHEpi<E, BM, BN>>(gemm_grid(g, pl.splits), stream, A, B, g, hp);
@@ -311,7 +341,8 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
         // ---- grad_W^T (+)= H_c^T G (M = d, N = V_pad, K = rc)
         {
             StageScope scope(KD_STAGE_GRAD_W, stream);
-            const Operand A = operand(Hc, pl.d, rc * pl.d * es);
+            // fused entry: G = fscale_t * stored values, so the operand is fscale_t * H_t
+            const Operand A = operand(fused ? static_cast<const char*>(Hs) : Hc, pl.d, rc * pl.d * es);
             const Operand B = g_operand(G, pl);
             const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 8);
             GradWParams wp{};
