@@ -63,15 +63,14 @@ __device__ __forceinline__ void dtl_load16(const u32x4& rsrc_in, uint32_t lds_ad
     u32x4 rsrc;
 #pragma unroll
     for (int w = 0; w < 4; ++w) rsrc[w] = (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc_in[w]);
-    uint32_t saved;   // m0 is restored, so the compiler's own uses of it are unaffected
+    // m0 is declared clobbered: the compiler keeps none of its own values in it
+    // across the block (and saves it only where it has one)
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
+        "s_mov_b32 m0, %2\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
         : "v"(voff), "s"(rsrc), "s"(lds_addr)
-        : "memory");
+        : "memory", "m0");
 }
 
 // Hides a per-lane value from loop-invariant code motion: the compiler would
@@ -150,7 +149,12 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, true, BLOCKED> {
     uint64_t tile_off;   // byte offset of this wave's first row of the tile
     uint32_t lrow;       // byte offset of this lane's row within an instruction's rows
     int zl;              // lane part of the chunk index
+    uint32_t voff[NI];   // this lane's byte offset for each instruction (the same every K step)
 
+    __device__ __forceinline__ int chunk(int i, int wave) const {
+        if constexpr (kCh == 8) return zl ^ i;
+        else return zl ^ (2 * ((wave * NI + i) & 1));
+    }
     __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
         op = o;
         tile_off = (uint64_t)m0 * (uint64_t)o.ld * 2u + (uint64_t)(wave * NI * RPI) * 2u * (uint64_t)o.ld;
@@ -158,6 +162,9 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, true, BLOCKED> {
         // k_swz of row RPI u + l / kCh without the part that depends on u
         if constexpr (kCh == 8) zl = (lane & 7) ^ (lane >> 3) ^ ((wave * NI) & 7);
         else zl = (lane & 3) ^ ((lane >> 3) & 3) ^ (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            voff[i] = lrow + (uint32_t)(i * RPI * 2 * o.ld) + (uint32_t)(chunk(i, wave) << 4);
     }
     __device__ __forceinline__ u32x4 rsrc(int k0) const {
         // blocked: ld = 64 and k0 lies in block k0 / 64
@@ -171,11 +178,8 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, true, BLOCKED> {
     // instruction i of the step at k0 into the tile at LDS byte address `tile`
     __device__ __forceinline__ void issue1(const u32x4& rs, uint32_t tile, int i, int k0, int kend, bool full,
                                            int wave) const {
-        int c;
-        if constexpr (kCh == 8) c = zl ^ i;
-        else c = zl ^ (2 * ((wave * NI + i) & 1));
-        uint32_t v = lrow + (uint32_t)(i * RPI * 2 * op.ld) + (uint32_t)(c << 4);
-        if (!full && k0 + c * 8 >= kend) v = kOOB;
+        uint32_t v = voff[i];
+        if (!full && k0 + chunk(i, wave) * 8 >= kend) v = kOOB;
         dtl_load16(rs, tile + (uint32_t)((wave * NI + i) * 1024), v);
     }
     // Fragment addresses: 32-row fragment f (rows base + 32 f ..) of sub-step
@@ -219,6 +223,7 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, false, BLOCKED> {
     int zl;              // lane part of the chunk index
     int kw;              // (w NI) / 4, whose parity enters the chunk swizzle
     int kl;              // this lane's k-row within an instruction (0 or 1)
+    uint32_t voff[NI];   // this lane's byte offset for each instruction (the same every K step)
 
     __device__ __forceinline__ void init(const Operand& o, int m0, int wave, int lane) {
         op = o;
@@ -228,6 +233,14 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, false, BLOCKED> {
         lrow = (uint32_t)(kl * krow());
         zl = (lane & 31) ^ (kl << 2);
         kw = (wave * NI) >> 2;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = zl ^ (8 * (i & 1)) ^ (16 * ((kw + (i >> 2)) & 1));
+            if constexpr (BLOCKED)
+                voff[i] = lrow + (uint32_t)(i * 2 * 128) + (uint32_t)(c >> 3) * (uint32_t)o.kblock + (uint32_t)((c & 7) << 4);
+            else
+                voff[i] = lrow + (uint32_t)(i * 4 * o.ld) + (uint32_t)(c << 4);
+        }
     }
     __device__ __forceinline__ u32x4 rsrc(int k0) const { return window_rsrc(op, tile_off + (uint64_t)k0 * krow()); }
     __device__ __forceinline__ void hide() {
@@ -237,12 +250,7 @@ template <int ROWS, bool BLOCKED> struct DtlLoader<ROWS, false, BLOCKED> {
     }
     __device__ __forceinline__ void issue1(const u32x4& rs, uint32_t tile, int i, int k0, int kend, bool full,
                                            int wave) const {
-        const int c = zl ^ (8 * (i & 1)) ^ (16 * ((kw + (i >> 2)) & 1));
-        uint32_t v;
-        if constexpr (BLOCKED)
-            v = lrow + (uint32_t)(i * 2 * 128) + (uint32_t)(c >> 3) * (uint32_t)op.kblock + (uint32_t)((c & 7) << 4);
-        else
-            v = lrow + (uint32_t)(i * 4 * op.ld) + (uint32_t)(c << 4);
+        uint32_t v = voff[i];
         if (!full && k0 + (wave * NI + i) * 2 + kl >= kend) v = kOOB;
         dtl_load16(rs, tile + (uint32_t)((wave * NI + i) * 1024), v);
     }
@@ -406,18 +414,22 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         p.tile = lds_addr_of(stage(step));
         return p;
     };
-    auto load1 = [&](const Pending& p, int q) {
-        if (q < LA::NI) la.issue1(p.ra, p.tile, q, p.k0, kend, p.full, wave);
-        else            lb.issue1(p.rb, p.tile + kDtlTile, q - LA::NI, p.k0, kend, p.full, wave);
+    // WHOLE: this workgroup's K range is a whole number of steps, so no load
+    // needs the K-tail check (compile-time, so the checks vanish)
+    auto load1 = [&](const Pending& p, int q, auto WHOLE) {
+        const bool full = decltype(WHOLE)::value || p.full;
+        if (q < LA::NI) la.issue1(p.ra, p.tile, q, p.k0, kend, full, wave);
+        else            lb.issue1(p.rb, p.tile + kDtlTile, q - LA::NI, p.k0, kend, full, wave);
     };
     // one MFMA group carrying load instructions first .. first + CNT - 1
-    auto group = [&](const Frags& f, auto with_loads, const Pending& p, auto first_c, auto cnt_c, auto fmv_c) {
+    auto group = [&](const Frags& f, auto with_loads, const Pending& p, auto first_c, auto cnt_c, auto fmv_c,
+                     auto WHOLE) {
         constexpr int first = decltype(first_c)::value, CNT = decltype(cnt_c)::value;
         constexpr int NQ = decltype(fmv_c)::value * FN;
         if constexpr (decltype(with_loads)::value && CNT > 0) {
             if constexpr (NQ == 0) {
 #pragma unroll
-                for (int t = 0; t < CNT; ++t) load1(p, first + t);
+                for (int t = 0; t < CNT; ++t) load1(p, first + t, WHOLE);
             } else {
                 // load t follows MFMA (t * NQ) / CNT
 #pragma unroll
@@ -426,7 +438,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int t = 0; t < CNT; ++t)
-                        if ((t * NQ) / CNT == q) load1(p, first + t);
+                        if ((t * NQ) / CNT == q) load1(p, first + t, WHOLE);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -439,7 +451,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     using Z = std::integral_constant<int, 0>;
 
     // Main loop of one wave; LOADS: this wave issues loads.
-    auto run = [&](auto LOADS, auto FMVc) {
+    auto run = [&](auto LOADS, auto FMVc, auto WHOLE) {
         constexpr bool loads = decltype(LOADS)::value;
         Frags f0, f1;
         if constexpr (loads) {
@@ -450,13 +462,13 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                 if (j < nk) {
                     const Pending p = pending_for(j);
 #pragma unroll
-                    for (int q = 0; q < NT; ++q) load1(p, q);
+                    for (int q = 0; q < NT; ++q) load1(p, q, WHOLE);
                 }
             }
             if (NS - 1 < nk) {
                 const Pending p = pending_for(NS - 1);
 #pragma unroll
-                for (int q = 0; q < kPost; ++q) load1(p, q);
+                for (int q = 0; q < kPost; ++q) load1(p, q, WHOLE);
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(kAhead + kPost, 15));   // step 0 landed
             } else {
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
@@ -489,10 +501,10 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                 using Cnt = std::integral_constant<int, hi - lo>;
                 if constexpr (s % 2 == 0) {
                     read(f1, cur, s + 1, FMVc);
-                    group(f0, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc);
+                    group(f0, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
                 } else {
                     read(f0, cur, s + 1, FMVc);
-                    group(f1, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc);
+                    group(f1, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
                 }
             });
             static_assert(SUB % 2 == 0, "the last sub-step uses the second register set");
@@ -505,7 +517,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
             }
             if constexpr (post) pq = pending_for(it + NS);
             // sub-step SUB - 1
-            group(f1, std::integral_constant<bool, post>{}, pq, Z{}, std::integral_constant<int, kPost>{}, FMVc);
+            group(f1, std::integral_constant<bool, post>{}, pq, Z{}, std::integral_constant<int, kPost>{}, FMVc, WHOLE);
         };
         const std::true_type yes{};
         const std::false_type no{};
@@ -522,13 +534,15 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         const int fmv = rem > 64 ? 4 : (rem > 0 ? 2 : 0);
         using F4 = std::integral_constant<int, 4>;
         using F2 = std::integral_constant<int, 2>;
-        auto dispatch = [&](auto LOADS) {
-            if (fmv == 4)      run(LOADS, F4{});
-            else if (fmv == 2) run(LOADS, F2{});
-            else               run(LOADS, Z{});
+        auto dispatch = [&](auto LOADS, auto WHOLE) {
+            if (fmv == 4)      run(LOADS, F4{}, WHOLE);
+            else if (fmv == 2) run(LOADS, F2{}, WHOLE);
+            else               run(LOADS, Z{}, WHOLE);
         };
-        if (loader) dispatch(std::true_type{});
-        else        dispatch(std::false_type{});
+        const bool whole = (kend - kbeg) % BK == 0;
+        if (!loader)    dispatch(std::false_type{}, std::false_type{});
+        else if (whole) dispatch(std::true_type{}, std::true_type{});
+        else            dispatch(std::true_type{}, std::false_type{});
     }
     __syncthreads();   // LDS is reused by epilogues
     Epi::apply(mma, m0, n0, split, wm, wn, lane, tid, smem, ep);
