@@ -64,9 +64,12 @@ __device__ __forceinline__ void dtl_load16(const u32x4& rsrc_in, uint32_t lds_ad
 #pragma unroll
     for (int w = 0; w < 4; ++w) rsrc[w] = (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc_in[w]);
     // m0 is declared clobbered: the compiler keeps none of its own values in it
-    // across the block (and saves it only where it has one)
+    // across the block (and saves it only where it has one).  An SALU write of
+    // m0 needs one wait state before an LDS-DMA load reads it (the compiler pads
+    // its own such sequences with s_nop 0 on this target).
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %0, %1, 0 offen lds"
         :
         : "v"(voff), "s"(rsrc), "s"(lds_addr)
