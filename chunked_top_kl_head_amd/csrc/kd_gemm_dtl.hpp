@@ -46,8 +46,13 @@ __device__ __forceinline__ u32x4 rsrc_words(uint64_t a, uint32_t bytes) {
 // every K step so that all per-lane offsets stay far below 2^31 whatever the
 // operand size.  Windows that start past the end get no records (all zeros).
 __device__ __forceinline__ u32x4 window_rsrc(const Operand& op, uint64_t off) {
-    const uint64_t rec = op.bytes > off ? op.bytes - off : 0;
-    return rsrc_words(reinterpret_cast<uint64_t>(op.ptr) + off, (uint32_t)(rec < 0x7FFFFFFFull ? rec : 0x7FFFFFFFull));
+    // records = clamp(bytes - off, 0, 2^31 - 1), with 32-bit compares only (the
+    // scalar unit has no 64-bit ordered compare)
+    const uint64_t diff = (uint64_t)op.bytes - off;
+    const int32_t hi = (int32_t)(diff >> 32);
+    const uint32_t lo = (uint32_t)diff;
+    const uint32_t rec = hi < 0 ? 0u : ((hi > 0 || lo > 0x7FFFFFFFu) ? 0x7FFFFFFFu : lo);
+    return rsrc_words(reinterpret_cast<uint64_t>(op.ptr) + off, rec);
 }
 
 // One direct-to-LDS load: lane l's 16 bytes at byte offset `voff` of the
@@ -379,21 +384,32 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
 #pragma unroll
             for (int e = 0; e < 16; ++e) mma.acc[i][j][e] = 0.f;
 
+    // LDS layout: the A tile of stage s at s * kDtlTile, its B tile at
+    // (NS + s) * kDtlTile.  The B fragment offsets carry the NS * kDtlTile, so
+    // both operands of stage s are read from the base s * kDtlTile plus a
+    // per-lane offset and a constant below 64 KiB: with the stage known at
+    // compile time (the main loop is unrolled NS times) the constant is the
+    // LDS instruction's immediate offset and no address is recomputed per step.
     typename LA::Frag fa = LA::frag_addr(wm * (BM / 2), lane);
     typename LB::Frag fb = LB::frag_addr(wn * (BN / WN), lane);
+#pragma unroll
+    for (int y = 0; y < (int)(sizeof(fb.off) / sizeof(int)); ++y) fb.off[y] += NS * kDtlTile;
     struct Frags {
         u32x4 a[FM], b[FN];
     };
-    auto stage = [&](int step) { return smem + (int)((unsigned)step % (unsigned)NS) * kDtlStage; };
+    auto a_tile = [&](int step) { return smem + (int)((unsigned)step % (unsigned)NS) * kDtlTile; };
+    auto b_tile = [&](int step) { return smem + (NS + (int)((unsigned)step % (unsigned)NS)) * kDtlTile; };
     // FMV: fragments of this wave's rows that hold output rows below M (the
-    // others are neither read nor multiplied)
-    auto read = [&](Frags& f, const lds_t* tile, int s, auto fmv_c) {
+    // others are neither read nor multiplied); ps: the stage (a constant in the
+    // unrolled main loop)
+    auto read = [&](Frags& f, int ps, int s, auto fmv_c) {
         constexpr int FMV = decltype(fmv_c)::value;
         if constexpr (FMV == 0) return;
+        const lds_t* base = smem + ps * kDtlTile;
 #pragma unroll
-        for (int i = 0; i < FMV; ++i) f.a[i] = LA::frag(tile, fa, i, s);
+        for (int i = 0; i < FMV; ++i) f.a[i] = LA::frag(base, fa, i, s);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) f.b[j] = LB::frag(tile + kDtlTile, fb, j, s);
+        for (int j = 0; j < FN; ++j) f.b[j] = LB::frag(base, fb, j, s);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto mfma1 = [&](const Frags& f, int q) {
@@ -404,7 +420,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     // the loads of one step
     struct Pending {
         u32x4 ra, rb;
-        uint32_t tile;
+        uint32_t tile, tileb;   // LDS byte addresses of the step's A and B tiles
         int k0;
         bool full;
     };
@@ -414,7 +430,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         p.full = p.k0 + BK <= kend;
         p.ra = la.rsrc(p.k0);
         p.rb = lb.rsrc(p.k0);
-        p.tile = lds_addr_of(stage(step));
+        p.tile = lds_addr_of(a_tile(step));
+        p.tileb = lds_addr_of(b_tile(step));
         return p;
     };
     // WHOLE: this workgroup's K range is a whole number of steps, so no load
@@ -422,7 +439,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     auto load1 = [&](const Pending& p, int q, auto WHOLE) {
         const bool full = decltype(WHOLE)::value || p.full;
         if (q < LA::NI) la.issue1(p.ra, p.tile, q, p.k0, kend, full, wave);
-        else            lb.issue1(p.rb, p.tile + kDtlTile, q - LA::NI, p.k0, kend, full, wave);
+        else            lb.issue1(p.rb, p.tileb, q - LA::NI, p.k0, kend, full, wave);
     };
     // one MFMA group carrying load instructions first .. first + CNT - 1
     auto group = [&](const Frags& f, auto with_loads, const Pending& p, auto first_c, auto cnt_c, auto fmv_c,
@@ -478,11 +495,11 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
             }
         }
         wave_barrier();
-        read(f0, smem, 0, FMVc);
+        read(f0, 0, 0, FMVc);
         // One K step.  PRE / POST: the groups before / after this step's
         // barrier carry loads of step it + NS - 1 / it + NS (compile-time, so
-        // the MFMA groups stay free of branches).
-        auto body = [&](auto PRE, auto POST, int it) {
+        // the MFMA groups stay free of branches); ps = it mod NS.
+        auto body = [&](auto PRE, auto POST, int it, int ps) {
             la.hide();
             lb.hide();
 #pragma unroll
@@ -491,7 +508,6 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
             for (int y = 0; y < (int)(sizeof(fb.off) / sizeof(int)); ++y) opaque(fb.off[y]);
             constexpr bool pre = decltype(PRE)::value && loads && kPre > 0;
             constexpr bool post = decltype(POST)::value && loads && kPost > 0;
-            const lds_t* cur = stage(it);
             Pending pp{}, pq{};
             if constexpr (pre) pp = pending_for(it + NS - 1);   // its stage is free since the last barrier
             // sub-steps 0 .. SUB - 2: read the next sub-step's fragments, then
@@ -503,10 +519,10 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                 using First = std::integral_constant<int, lo>;
                 using Cnt = std::integral_constant<int, hi - lo>;
                 if constexpr (s % 2 == 0) {
-                    read(f1, cur, s + 1, FMVc);
+                    read(f1, ps, s + 1, FMVc);
                     group(f0, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
                 } else {
-                    read(f0, cur, s + 1, FMVc);
+                    read(f0, ps, s + 1, FMVc);
                     group(f1, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
                 }
             });
@@ -515,8 +531,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                 // this wave's loads of step it + 1 and its reads of `cur` are complete
                 if constexpr (decltype(PRE)::value) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kAhead, 0));
                 else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-                wave_barrier();                       // every wave's loads landed; `cur` is free
-                read(f0, stage(it + 1), 0, FMVc);
+                wave_barrier();                       // every wave's loads landed; stage ps is free
+                read(f0, ps + 1 == NS ? 0 : ps + 1, 0, FMVc);
             }
             if constexpr (post) pq = pending_for(it + NS);
             // sub-step SUB - 1
@@ -524,10 +540,16 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         };
         const std::true_type yes{};
         const std::false_type no{};
+        auto stage_of = [&](int it) { return (int)((unsigned)it % (unsigned)NS); };
         int it = 0;
-        for (; it + NS < nk; ++it) body(yes, yes, it);
-        if (it + NS - 1 < nk) body(yes, no, it++);
-        for (; it < nk; ++it) body(no, no, it);
+        for (; it + 2 * NS - 1 < nk; it += NS)
+            static_for<NS>([&](auto P) { body(yes, yes, it + decltype(P)::value, decltype(P)::value); });
+        for (; it + NS < nk; ++it) body(yes, yes, it, stage_of(it));
+        if (it + NS - 1 < nk) {
+            body(yes, no, it, stage_of(it));
+            ++it;
+        }
+        for (; it < nk; ++it) body(no, no, it, stage_of(it));
     };
     if (nk > 0) {
         // rows of this wave's half below M: all (4 fragments), at most 64 (2)
