@@ -202,7 +202,8 @@ def test_duplicate_ids_and_upstream_gradient(oracle):
         check_against(ref, out[path], tol_for("bf16"), x, path)
 
 
-def test_rows_far_above_their_cached_logits(oracle):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rows_far_above_their_cached_logits(oracle, dtype):
     """Rows whose largest student logit lies far above every cached id's.
 
     The fused entry stores each 128-id block's exponentials relative to the
@@ -211,7 +212,7 @@ def test_rows_far_above_their_cached_logits(oracle):
     as W_v = a H_t (v outside row t's cache) lifts z_tv to a |H_t|^2:
     a = 0.2 gives ~92 (base 2) above the cached logits (rescaled rows), a = 0.12
     ~55 (stored values up to ~2^55 on the common path)."""
-    x = synth.make_inputs(300, 320, 3000, 20, tau=1.0, dtype="bf16", seed=109, mask=("random", 0.1))
+    x = synth.make_inputs(300, 320, 3000, 20, tau=1.0, dtype=dtype, seed=109, mask=("random", 0.1))
     kept = np.nonzero(x.ignore == 0)[0]
     plant = [(int(kept[0]), 0.2), (int(kept[40]), 0.2), (int(kept[-1]), 0.2), (int(kept[100]), 0.12),
              (int(kept[150]), 0.12)]
@@ -221,9 +222,12 @@ def test_rows_far_above_their_cached_logits(oracle):
         v = next(v for v in range(x.V - 1, -1, -1) if v not in set(x.topk_idx[t].tolist()) and v not in used)
         used.add(v)
         W[v] = a * x.H[t]
-    bits = synth.f32_to_bf16_bits(W.astype(np.float32))
-    x.W_bits[:] = bits.reshape(x.W_bits.shape)
-    x.W[:] = synth.bf16_bits_to_f32(bits).reshape(x.W.shape)
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(W.astype(np.float32))
+        x.W_bits[:] = bits.reshape(x.W_bits.shape)
+        x.W[:] = synth.bf16_bits_to_f32(bits).reshape(x.W.shape)
+    else:
+        x.W[:] = W
     ref = oracle.full(x.H, x.W, x.topk_idx, x.topk_logit, x.ignore, tau=1.0)
     gap = [(ref["lse"][t] - np.max(x.H[t].astype(np.float64) @ x.W[x.topk_idx[t]].astype(np.float64).T)) / np.log(2)
            for t, _ in plant]
@@ -231,7 +235,7 @@ def test_rows_far_above_their_cached_logits(oracle):
     assert min(gap[:3]) > 70 and 40 < min(gap[3:]) < 64
     out = run_all_paths(upload(x), 1.0, 128)
     for path in ("fused", "split"):
-        check_against(ref, out[path], tol_for("bf16"), x, path)
+        check_against(ref, out[path], tol_for(dtype), x, path)
 
 
 def test_validate_counts_bad_cache():
