@@ -46,14 +46,16 @@ template <typename E> struct GLayout {
 // ---------------------------------------------------------------------------
 // Logit-tile epilogue: the tile is Z^T (rows = vocabulary ids v, columns =
 // chunk rows t).  Each wave reduces its own 128 ids of a column to a partial
-// (max, sum of exp) in base 2, so a 256-id tile leaves two partials per row
-// and no wave waits for another -- the online logsumexp of [TH] "Fused
-// chunked KL" is this blocked max/sum plus a merge in the row kernel.
+// (reference R, sum of 2^(y - R)) in base 2, so a 256-id tile leaves two
+// partials per row and no wave waits for another -- the online logsumexp of
+// [TH] "Fused chunked KL" is this blocked reduction plus a merge in the row
+// kernel.  R is the row's R0 (from the row kernel's first pass) unless the
+// block's max lies more than kRefSlack above it.
 //   kStats: write the partials only (forward).
-//   kFused: also write e = exp2(y - block max) as the MFMA operand of the
-//           gradient GEMMs (rescaled to G in place by the row kernel).
+//   kFused: also write e = 2^(y - R) as the MFMA operand of the gradient GEMMs
+//           (G = one factor per row times e; see the row kernel).
 //   kBwd  : lse is known: write the dense part of G, s * exp(a - lse), directly.
-constexpr int kStatIds = 128;   // vocabulary ids per (max, sum) partial
+constexpr int kStatIds = 128;   // vocabulary ids per partial
 // ---------------------------------------------------------------------------
 struct LogitsParams {
     f32x2* stats;          // [C][nst] (max2, sum) per (row, 128-id block)

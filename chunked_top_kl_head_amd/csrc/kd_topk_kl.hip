@@ -9,12 +9,17 @@
 // recomputes them, and memory grows linearly with the sequence length.
 //
 // Per chunk of C rows the scheduler enqueues, on the caller's stream:
-//   forward : logits GEMM (tile max/sum partials) -> row kernel (lse, teacher,
-//             gather, row loss) -> chunk loss sum
+//   forward : row kernel (cached-id logits, row references) -> logits GEMM
+//             (block partials) -> row kernel (lse, teacher, row loss) -> chunk
+//             loss sum
 //   backward: logits GEMM recomputed with the forward's lse (dense G) -> row
 //             kernel (cached-id entries of G) -> grad_H GEMM -> grad_W GEMM
-//   fused   : logits GEMM (partials + softmax numerators) -> row kernel (lse,
-//             loss, G in place) -> grad_H GEMM -> grad_W GEMM
+//   fused   : row kernel (cached-id logits, references) -> logits GEMM
+//             (partials + softmax numerators relative to the references) ->
+//             row kernel (lse, loss, row factors, cached entries) -> rescale of
+//             rows whose references moved (usually none) -> cached entries
+//             into G -> row-scaled H_c -> grad_H GEMM (row factors in its
+//             epilogue) -> grad_W GEMM (on the row-scaled H_c)
 // The workspace holds one chunk's G (C x V_pad) and partials, so its size is
 // independent of T; the T-sized arrays are the caller's inputs and outputs.
 #include <hip/hip_runtime.h>
