@@ -61,6 +61,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Combine lanes l and l ^ 32 with one VALU swap of the two 32-lane halves
+// (v_permlane32_swap) instead of an LDS permute: x[l] and x[l ^ 32] end up in
+// the two results, in some order, on every lane.
+__device__ __forceinline__ float halves_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // LDS operand tiles are ROWS x 128 bytes (one row = 128 bytes of the K
 // extent).  The 16-byte chunk c of row r lives at chunk position
 // c ^ ((r ^ (r >> 3)) & 7): rows that differ in their low three bits, or in

@@ -569,7 +569,9 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
         else if (whole) dispatch(std::true_type{}, std::true_type{});
         else            dispatch(std::true_type{}, std::false_type{});
     }
-    __syncthreads();   // LDS is reused by epilogues
+    // An epilogue that reuses the stage LDS synchronises the workgroup itself
+    // before its first LDS write (other waves may still be reading fragments);
+    // work before that point overlaps the other waves' last MFMAs.
     Epi::apply(mma, m0, n0, split, wm, wn, lane, tid, smem, ep);
 }
 

@@ -125,12 +125,28 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
     // The accumulators hold raw logits z; base-2 values are y = z * scale2
     // (scale2 = log2(e) / tau > 0), formed inside the exponent with one fma.
     // Ids at or beyond V (the padding of the last vocabulary tile only) are
-    // excluded as -inf.
+    // excluded as -inf.  The values are computed in place in the accumulators;
+    // the staged path synchronises the workgroup only before its first LDS
+    // write (other waves may still be reading their last fragments).
     template <class Mma>
     static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int /*split*/, int wm, int wn,
                                                  int lane, int tid, lds_t* smem, const Params& p) {
         constexpr int FM = Mma::FM, FN = Mma::FN;
         const float sc = p.scale2;
+        // per-column inputs, all requested before any of them is needed
+        float colv[FN];
+        bool kept[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int t = n0 + Mma::col(wn, j, lane);
+            const bool live = t < p.rows;
+            if constexpr (MODE == kBwd) {
+                colv[j] = live ? p.lse[t] : 0.f;
+                kept[j] = live && ((p.ignore == nullptr) || (p.ignore[t] == 0));
+            } else {
+                colv[j] = live ? p.ref[t] : -INFINITY;
+            }
+        }
         if (m0 + BM > p.V) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -151,29 +167,14 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
             const float s = p.hdr->s;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int t = n0 + Mma::col(wn, j, lane);
-                const bool live = t < p.rows;
-                const bool kept = live && ((p.ignore == nullptr) || (p.ignore[t] == 0));
-                const float st = kept ? s : 0.f;
-                const float l2 = live ? p.lse[t] * kLog2e : 0.f;
+                const float st = kept[j] ? s : 0.f;
+                const float l2 = colv[j] * kLog2e;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float g[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) g[r] = st * fast_exp2(fmaf(mma.acc[i][j][4 * q + r], sc, -l2));
-                        if constexpr (kStaged)
-                            stage_write4<Mma>(smem, wm, wn, i, j, q, lane, g[0], g[1], g[2], g[3]);
-                        else if (live)
-                            store4(p, t, m0 + Mma::row(wm, i, q, lane), g[0], g[1], g[2], g[3]);
-                    }
+                    for (int e = 0; e < 16; ++e)
+                        mma.acc[i][j][e] = st * fast_exp2(fmaf(mma.acc[i][j][e], sc, -l2));
             }
-            if constexpr (kStaged) {
-                __syncthreads();
-                stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.C, n0, m0, p.rows, tid);
-            }
-            return;
         } else {
             // this wave's 128 ids of each of its columns (lanes l and l + 32
             // hold the same column): max, then exp2 relative to a reference and
@@ -189,13 +190,10 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) mz = fmaxf(mz, mma.acc[i][j][e]);
-                mz = fmaxf(mz, __shfl_xor(mz, 32, kWave));
+                mz = halves_max(mz);
                 const int t = n0 + Mma::col(wn, j, lane);
                 float my = mz * sc;
-                {
-                    const float r0 = t < p.rows ? p.ref[t] : -INFINITY;
-                    my = my <= r0 + kRefSlack ? r0 : my;
-                }
+                my = my <= colv[j] + kRefSlack ? colv[j] : my;
                 // every id of the block beyond V (kStats) or no reference: all
                 // terms are exp2(-inf) = 0
                 const float off = my == -INFINITY ? 0.f : my;
@@ -208,35 +206,36 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
                         mma.acc[i][j][e] = x;
                         sum += x;
                     }
-                sum += __shfl_xor(sum, 32, kWave);
+                sum = halves_sum(sum);
                 if (lane < 32 && t < p.rows)
                     p.stats[(int64_t)t * p.nst + (m0 / BM) * 2 + wm] = f32x2{my, sum};
             }
-            if constexpr (MODE == kFused) {
-                if constexpr (kStaged) {
+        }
+        if constexpr (MODE != kStats) {
+            if constexpr (kStaged) {
+                __syncthreads();   // every wave is past its main loop: the stage LDS is free
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-                        for (int i = 0; i < FM; ++i)
+                    for (int i = 0; i < FM; ++i)
 #pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                stage_write4<Mma>(smem, wm, wn, i, j, q, lane, mma.acc[i][j][4 * q],
-                                                  mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
-                                                  mma.acc[i][j][4 * q + 3]);
-                    __syncthreads();
-                    stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.C, n0, m0, p.rows, tid);
-                } else {
+                        for (int q = 0; q < 4; ++q)
+                            stage_write4<Mma>(smem, wm, wn, i, j, q, lane, mma.acc[i][j][4 * q],
+                                              mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
+                                              mma.acc[i][j][4 * q + 3]);
+                __syncthreads();
+                stage_flush(smem, reinterpret_cast<uint16_t*>(p.E), p.C, n0, m0, p.rows, tid);
+            } else {
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        const int t = n0 + Mma::col(wn, j, lane);
-                        if (t >= p.rows) continue;
+                for (int j = 0; j < FN; ++j) {
+                    const int t = n0 + Mma::col(wn, j, lane);
+                    if (t >= p.rows) continue;
 #pragma unroll
-                        for (int i = 0; i < FM; ++i)
+                    for (int i = 0; i < FM; ++i)
 #pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                store4(p, t, m0 + Mma::row(wm, i, q, lane), mma.acc[i][j][4 * q],
-                                       mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]);
-                    }
+                        for (int q = 0; q < 4; ++q)
+                            store4(p, t, m0 + Mma::row(wm, i, q, lane), mma.acc[i][j][4 * q],
+                                   mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]);
                 }
             }
         }
@@ -329,6 +328,7 @@ template <typename E, int BM, int BN> struct GradWEpi {
             f32x4 old[NK];
 #pragma unroll
             for (int k = 0; k < NK; ++k) old[k] = load_old(0, k);
+            __syncthreads();   // every wave is past its main loop: the stage LDS is free
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int h = m0 + 128 * half + 4 * c;
