@@ -739,47 +739,23 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
 
 // Fused entry, dirty rows only: stored value *= 2^(R_b - Mall) per 128-id
 // block (the factors the row kernel left in the block statistics), in place,
-// over the chunk's G buffer in its physical order.  Each workgroup streams
-// kRescaleSpan contiguous 16-byte chunks: bf16 (blocked layout) grid =
-// (C * 8 / span, V_pad / 64), one 64-id block per grid row; fp32 (row-major)
-// grid = (C, V_pad / 4 / span), one row per grid column.  When no row of the
-// chunk is dirty every workgroup exits at once.
+// over the chunk's G buffer in its physical order.  The buffer is cut into
+// spans of kRescaleSpan contiguous 16-byte chunks: bf16 (blocked layout)
+// span (sx, sy) = chunks sx * span .. of 64-id block sy, nx = C * 8 / span;
+// fp32 (row-major) span (sx, sy) = row sx, chunks sy * span .., nx = C.  A
+// grid of at most kRescaleGrid workgroups strides over the spans, so that a
+// chunk with no dirty row (the usual case) costs one small launch whose
+// workgroups all exit at once.
 constexpr int kRescaleU = 8;                          // chunks in flight per thread
-constexpr int kRescaleSpan = kThreads * kRescaleU;    // chunks per workgroup
+constexpr int kRescaleSpan = kThreads * kRescaleU;    // chunks per span
+constexpr int kRescaleGrid = 1024;
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void rescale_kernel(void* G, const f32x2* fac, const uint8_t* dirty,
-                                                           const WsHeader* hdr, int nst, int C, int V_pad, int rows) {
+                                                           const WsHeader* hdr, int nst, int C, int V_pad, int rows,
+                                                           int nx, int64_t nspans) {
     if (hdr->dirty == 0) return;
     constexpr int kEpc = 16 / Elem<E>::size;          // elements per 16-byte chunk
-    int64_t base;                                     // first chunk of this workgroup
-    int64_t end;                                      // end of its contiguous range
-    int r0, v0;                                       // (row, id) of chunk `base`
-    if constexpr (GLayout<E>::kBlocked) {
-        const int per_blk = C * (kGBlock / kEpc);     // chunks of one 64-id block
-        const int w0 = (int)blockIdx.x * kRescaleSpan;
-        base = (int64_t)blockIdx.y * per_blk + w0;
-        end = (int64_t)blockIdx.y * per_blk + min(per_blk, w0 + kRescaleSpan);
-        r0 = w0 / (kGBlock / kEpc);
-        v0 = (int)blockIdx.y * kGBlock;
-    } else {
-        const int per_row = V_pad / kEpc;
-        const int w0 = (int)blockIdx.y * kRescaleSpan;
-        base = (int64_t)blockIdx.x * per_row + w0;
-        end = (int64_t)blockIdx.x * per_row + min(per_row, w0 + kRescaleSpan);
-        r0 = (int)blockIdx.x;
-        v0 = w0 * kEpc;
-    }
-    // chunk base + w -> (row, id)
-    auto where = [&](int w, int& r, int& v) {
-        if constexpr (GLayout<E>::kBlocked) {
-            r = r0 + w / (kGBlock / kEpc);
-            v = v0 + (w % (kGBlock / kEpc)) * kEpc;
-        } else {
-            r = r0;
-            v = v0 + w * kEpc;
-        }
-    };
     auto scale = [&](u32x4& x, float f) {
         if constexpr (Elem<E>::size == 2) {
 #pragma unroll
@@ -791,23 +767,54 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(void* G, const f32x2*
         }
     };
     u32x4* g = reinterpret_cast<u32x4*>(G);
-    u32x4 x[kRescaleU];
-    float f[kRescaleU];
-    bool live[kRescaleU];
+    for (int64_t sp = blockIdx.x; sp < nspans; sp += gridDim.x) {
+        const int sx = (int)(sp % nx), sy = (int)(sp / nx);
+        int64_t base;                                 // first chunk of this span
+        int64_t end;                                  // end of its contiguous range
+        int r0, v0;                                   // (row, id) of chunk `base`
+        if constexpr (GLayout<E>::kBlocked) {
+            const int per_blk = C * (kGBlock / kEpc); // chunks of one 64-id block
+            const int w0 = sx * kRescaleSpan;
+            base = (int64_t)sy * per_blk + w0;
+            end = (int64_t)sy * per_blk + min(per_blk, w0 + kRescaleSpan);
+            r0 = w0 / (kGBlock / kEpc);
+            v0 = sy * kGBlock;
+        } else {
+            const int per_row = V_pad / kEpc;
+            const int w0 = sy * kRescaleSpan;
+            base = (int64_t)sx * per_row + w0;
+            end = (int64_t)sx * per_row + min(per_row, w0 + kRescaleSpan);
+            r0 = sx;
+            v0 = w0 * kEpc;
+        }
+        // chunk base + w -> (row, id)
+        auto where = [&](int w, int& r, int& v) {
+            if constexpr (GLayout<E>::kBlocked) {
+                r = r0 + w / (kGBlock / kEpc);
+                v = v0 + (w % (kGBlock / kEpc)) * kEpc;
+            } else {
+                r = r0;
+                v = v0 + w * kEpc;
+            }
+        };
+        u32x4 x[kRescaleU];
+        float f[kRescaleU];
+        bool live[kRescaleU];
 #pragma unroll
-    for (int u = 0; u < kRescaleU; ++u) {
-        const int w = u * kThreads + (int)threadIdx.x;
-        int r, v;
-        where(w, r, v);
-        live[u] = base + w < end && r < rows && dirty[r] != 0;
-        f[u] = live[u] ? fac[(int64_t)r * nst + v / kStatIds][0] : 0.f;
-        x[u] = live[u] ? g[base + w] : u32x4{0u, 0u, 0u, 0u};
-    }
+        for (int u = 0; u < kRescaleU; ++u) {
+            const int w = u * kThreads + (int)threadIdx.x;
+            int r, v;
+            where(w, r, v);
+            live[u] = base + w < end && r < rows && dirty[r] != 0;
+            f[u] = live[u] ? fac[(int64_t)r * nst + v / kStatIds][0] : 0.f;
+            x[u] = live[u] ? g[base + w] : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-    for (int u = 0; u < kRescaleU; ++u) {
-        if (!live[u]) continue;
-        scale(x[u], f[u]);
-        g[base + u * kThreads + (int)threadIdx.x] = x[u];
+        for (int u = 0; u < kRescaleU; ++u) {
+            if (!live[u]) continue;
+            scale(x[u], f[u]);
+            g[base + u * kThreads + (int)threadIdx.x] = x[u];
+        }
     }
 }
 

@@ -305,11 +305,12 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
                 // dirty rows only: every block brought to the row's largest
                 // reference; then the cached entries; then the row-scaled H_c
                 const int epc = 16 / es;
-                const dim3 rg = es == 2 ? dim3((unsigned)cdiv(pl.C * (kGBlock / epc), (int64_t)kRescaleSpan),
-                                               (unsigned)(pl.V_pad / kGBlock))
-                                        : dim3((unsigned)pl.C, (unsigned)cdiv(pl.V_pad / epc, (int64_t)kRescaleSpan));
-                hipLaunchKernelGGL(rescale_kernel<E>, rg, dim3(kThreads), 0, stream, G, stats, dirty, hdr,
-                                   (int)pl.nst, (int)pl.C, (int)pl.V_pad, (int)rc);
+                const int64_t nx = es == 2 ? cdiv(pl.C * (kGBlock / epc), (int64_t)kRescaleSpan) : pl.C;
+                const int64_t ny = es == 2 ? pl.V_pad / kGBlock : cdiv(pl.V_pad / epc, (int64_t)kRescaleSpan);
+                const int64_t nspans = nx * ny;
+                hipLaunchKernelGGL(rescale_kernel<E>, dim3((unsigned)std::min<int64_t>(nspans, kRescaleGrid)),
+                                   dim3(kThreads), 0, stream, G, stats, dirty, hdr, (int)pl.nst, (int)pl.C,
+                                   (int)pl.V_pad, (int)rc, (int)nx, nspans);
                 const int64_t n = rc * pl.K;
                 hipLaunchKernelGGL(sparse_kernel<E>, dim3((unsigned)cdiv(n, (int64_t)kThreads)), dim3(kThreads), 0,
                                    stream, G, rp.sparse, n, (int)pl.K, (int)pl.C, (int)pl.V_pad);
