@@ -516,7 +516,9 @@ __device__ __forceinline__ float dot_row(const E* h, const E* w, int d, int lane
 // The wave's share of the K dot products H_t . W_id (bf16 rows of nc 16-byte
 // chunks, NR >= ceil(nc / 64) chunks per lane): the H row stays in registers,
 // and NP W rows are loaded before any of them is multiplied (NP = 2 measured
-// best: 3 and 4 lose more to occupancy than they gain).  Writes z / tau.
+// best: 3 and 4 lose more to occupancy than they gain).  Each packed pair of
+// bf16 products is added to the fp32 sum by one v_dot2 (the products of bf16
+// values are exact in fp32).  Writes z / tau.
 template <int NR>
 __device__ __forceinline__ void dots_bf16(const void* h, const void* W, const int* ids, int K, int d, int nc,
                                           int wave, int lane, float inv_tau, float* out) {
@@ -549,8 +551,11 @@ __device__ __forceinline__ void dots_bf16(const void* h, const void* W, const in
             for (int r = 0; r < NR; ++r)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc = fmaf(bf16_bits_to_f32(a[r][q] & 0xFFFFu), bf16_bits_to_f32(b[j][r][q] & 0xFFFFu), acc);
-                    acc = fmaf(bf16_bits_to_f32(a[r][q] >> 16), bf16_bits_to_f32(b[j][r][q] >> 16), acc);
+                    // scalar copies first: bit-casting the vector elements in
+                    // place compiled to one register read for all four q
+                    const uint32_t x = a[r][q], y = b[j][r][q];
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y),
+                                                          acc, false);
                 }
             const float z = wave_sum(acc);
             const int kk = k + j * NW;
