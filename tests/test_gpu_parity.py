@@ -202,26 +202,40 @@ def test_duplicate_ids_and_upstream_gradient(oracle):
         check_against(ref, out[path], tol_for("bf16"), x, path)
 
 
+# (T, d, V, K, chunk, kept-row positions of the five planted rows).  "wide":
+# a vocabulary of 70,000 ids cuts G into more spans than the rescale pass's
+# grid has workgroups (1,024), so its workgroups stride over spans (bf16:
+# ids from 65,536 on; fp32: each row's last span), and the last planted row
+# sits in the second chunk.
+RESCALE_CASES = {
+    "narrow": (300, 320, 3000, 20, 128, (0, 40, -1, 100, 150)),
+    "wide": (150, 64, 70000, 20, 128, (0, 40, -1, 60, 90)),
+}
+
+
+@pytest.mark.parametrize("case", list(RESCALE_CASES))
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_rows_far_above_their_cached_logits(oracle, dtype):
+def test_rows_far_above_their_cached_logits(oracle, dtype, case):
     """Rows whose largest student logit lies far above every cached id's.
 
     The fused entry stores each 128-id block's exponentials relative to the
     row's largest cached-id logit unless the block's own max exceeds it by more
     than 64 (base 2); such rows take the rescale path.  A vocabulary row planted
     as W_v = a H_t (v outside row t's cache) lifts z_tv to a |H_t|^2:
-    a = 0.2 gives ~92 (base 2) above the cached logits (rescaled rows), a = 0.12
+    z = 64 puts it ~92 (base 2) above the cached logits (rescaled rows), z = 38
     ~55 (stored values up to ~2^55 on the common path)."""
-    x = synth.make_inputs(300, 320, 3000, 20, tau=1.0, dtype=dtype, seed=109, mask=("random", 0.1))
+    T, d, V, K, chunk, at = RESCALE_CASES[case]
+    x = synth.make_inputs(T, d, V, K, tau=1.0, dtype=dtype, seed=109, mask=("random", 0.1))
     kept = np.nonzero(x.ignore == 0)[0]
-    plant = [(int(kept[0]), 0.2), (int(kept[40]), 0.2), (int(kept[-1]), 0.2), (int(kept[100]), 0.12),
-             (int(kept[150]), 0.12)]
+    plant = [(int(kept[at[0]]), 64.0), (int(kept[at[1]]), 64.0), (int(kept[at[2]]), 64.0),
+             (int(kept[at[3]]), 38.0), (int(kept[at[4]]), 38.0)]
     used = set()
     W = x.W.copy()
-    for t, a in plant:
+    for t, z in plant:
         v = next(v for v in range(x.V - 1, -1, -1) if v not in set(x.topk_idx[t].tolist()) and v not in used)
         used.add(v)
-        W[v] = a * x.H[t]
+        h = x.H[t].astype(np.float64)
+        W[v] = (z / float(h @ h)) * x.H[t]
     if dtype == "bf16":
         bits = synth.f32_to_bf16_bits(W.astype(np.float32))
         x.W_bits[:] = bits.reshape(x.W_bits.shape)
@@ -233,7 +247,7 @@ def test_rows_far_above_their_cached_logits(oracle, dtype):
            for t, _ in plant]
     say("planted rows, lse above the best cached logit (base 2): " + " ".join(f"{g:.0f}" for g in gap))
     assert min(gap[:3]) > 70 and 40 < min(gap[3:]) < 64
-    out = run_all_paths(upload(x), 1.0, 128)
+    out = run_all_paths(upload(x), 1.0, chunk)
     for path in ("fused", "split"):
         check_against(ref, out[path], tol_for(dtype), x, path)
 
