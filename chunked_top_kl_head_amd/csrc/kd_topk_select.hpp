@@ -15,7 +15,9 @@
 // One workgroup per row; the row is streamed from HBM about once:
 //   1. a 12-bit histogram of the keys of every 16th 128-byte line gives a
 //      lower bound L expected to leave a few hundred candidates;
-//   2. one pass over the row appends every key >= L to an LDS buffer;
+//   2. one pass over the row appends every key >= L to an LDS buffer (for a
+//      non-negative bound, whole 16-byte vectors below it are skipped after
+//      one integer max);
 //   3. if the count is in [K, capacity] the buffer is sorted (bitonic) and the
 //      first K are written; otherwise an exact radix select over the full row
 //      (8-bit digits of the 64-bit key, one pass per digit) finds a bound
@@ -108,6 +110,64 @@ __device__ __forceinline__ void sel_for_row(const void* row, int V, int tid, F&&
     for (int i = head + nv * N + tid; i < V; i += kSelThreads) f(sel_key(SelVec<E>::bits1(row, i)), i);
 }
 
+// Prefilter of the collection pass for bounds L >= 2^63 (a non-negative
+// value): an element can have a key >= L only if it is non-negative and its
+// bit pattern, read as a signed integer of the element's width, is at least
+// the pattern of the bound's top 32 key bits -- for non-negative values the
+// signed order of the patterns is the value order, negative values read as
+// negative integers.  A 16-byte vector whose largest such integer is below
+// that threshold holds no candidate; any other vector goes through the exact
+// per-element key test (which also rejects a NaN that passed the filter).
+template <typename E> struct SelFilter;
+template <> struct SelFilter<bf16_t> {
+    typedef __attribute__((ext_vector_type(2))) short s16x2;
+    static __device__ __forceinline__ s16x2 halves(uint32_t w) { return __builtin_bit_cast(s16x2, w); }
+    static __device__ __forceinline__ int vmax(const u32x4& v) {
+        // scalar copies first: bit-casting the vector elements in place
+        // compiles to one register read for all four
+        const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+        const s16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(halves(w0), halves(w1)),
+                                                  __builtin_elementwise_max(halves(w2), halves(w3)));
+        return m[0] > m[1] ? (int)m[0] : (int)m[1];
+    }
+    static __device__ __forceinline__ int threshold(uint32_t key32) { return (int)((key32 & 0x7FFFFFFFu) >> 16); }
+};
+template <> struct SelFilter<float> {
+    static __device__ __forceinline__ int vmax(const u32x4& v) {
+        return max(max((int)v[0], (int)v[1]), max((int)v[2], (int)v[3]));
+    }
+    static __device__ __forceinline__ int threshold(uint32_t key32) { return (int)(key32 & 0x7FFFFFFFu); }
+};
+
+// sel_for_row restricted to the vectors that pass the prefilter (threshold
+// thr); the head and tail elements are always visited.
+template <typename E, class F>
+__device__ __forceinline__ void sel_for_row_filtered(const void* row, int V, int tid, int thr, F&& f) {
+    constexpr int N = SelVec<E>::N;
+    const int head = sel_head<E>(row, V);
+    for (int i = tid; i < head; i += kSelThreads) f(sel_key(SelVec<E>::bits1(row, i)), i);
+    const u32x4* vec = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(row) + head * (int)sizeof(E));
+    const int nv = (V - head) / N;
+    auto visit = [&](const u32x4& v, int c) {
+        if (SelFilter<E>::vmax(v) < thr) return;
+        uint32_t u[N];
+        SelVec<E>::bits(v, u);
+#pragma unroll
+        for (int e = 0; e < N; ++e) f(sel_key(u[e]), head + c * N + e);
+    };
+    constexpr int U = 8;   // 16-byte loads in flight per thread
+    int c = tid;
+    for (; c + (U - 1) * kSelThreads < nv; c += U * kSelThreads) {
+        u32x4 v[U];
+#pragma unroll
+        for (int w = 0; w < U; ++w) v[w] = vec[c + w * kSelThreads];
+#pragma unroll
+        for (int w = 0; w < U; ++w) visit(v[w], c + w * kSelThreads);
+    }
+    for (; c < nv; c += kSelThreads) visit(vec[c], c);
+    for (int i = head + nv * N + tid; i < V; i += kSelThreads) f(sel_key(SelVec<E>::bits1(row, i)), i);
+}
+
 __device__ __forceinline__ uint64_t sel_full(uint32_t key, int id) {
     return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
 }
@@ -190,13 +250,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const void* lo
 
     // 2. collect every key >= bound
     auto collect = [&](uint64_t L) {
-        sel_for_row<E>(row, V, tid, [&](uint32_t key, int id) {
+        auto take = [&](uint32_t key, int id) {
             const uint64_t k = sel_full(key, id);
             if (k >= L) {
                 const uint32_t pos = atomicAdd(&count, 1u);
                 if (pos < (uint32_t)kSelCap) cand[pos] = k;
             }
-        });
+        };
+        if (L >> 63) sel_for_row_filtered<E>(row, V, tid, SelFilter<E>::threshold((uint32_t)(L >> 32)), take);
+        else         sel_for_row<E>(row, V, tid, take);
         __syncthreads();
     };
     collect(bound);
