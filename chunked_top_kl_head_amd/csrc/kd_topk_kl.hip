@@ -135,7 +135,8 @@ static kd_status check_problem(const kd_problem* p) {
     if (p->T < 0 || p->d < 1 || p->V < 1 || p->K < 1 || p->K > p->V || p->chunk < 0) return KD_ERR_SHAPE;
     if (!std::isfinite(p->temperature) || !(p->temperature > 0.f)) return KD_ERR_VALUE;
     if (p->dtype != KD_BF16 && p->dtype != KD_F32) return KD_ERR_UNSUPPORTED;
-    if (p->d % 8 != 0 || p->K > kMaxK || p->V > ((int64_t)1 << 21)) return KD_ERR_UNSUPPORTED;
+    // positions and ids are 32-bit inside the kernels
+    if (p->d % 8 != 0 || p->K > kMaxK || p->V > ((int64_t)1 << 21) || p->T > 0x7FFFFFFFLL) return KD_ERR_UNSUPPORTED;
     if ((p->flags & ~(KD_FLAG_ACCUMULATE_GRAD_W | KD_FLAG_LOGIT_BF16)) != 0 || p->reserved != 0) return KD_ERR_VALUE;
     return KD_OK;
 }

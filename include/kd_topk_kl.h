@@ -80,7 +80,8 @@ typedef enum {
     KD_ERR_VALUE = 3,        /* temperature not finite or <= 0, unknown flags, reserved != 0 */
     KD_ERR_ALIGN = 4,        /* a pointer violates the alignment above */
     KD_ERR_WORKSPACE = 5,    /* workspace_bytes below kd_topk_kl_workspace_size */
-    KD_ERR_UNSUPPORTED = 6,  /* dtype unknown, d % 8 != 0, K > 1024, or sizes beyond the 2^31-byte operand limit */
+    KD_ERR_UNSUPPORTED = 6,  /* dtype unknown, d % 8 != 0, K > 1024, V > 2^21, T >= 2^31, chunk or d > 2^20,
+                                or (fp32) an operand beyond 2^31 bytes */
     KD_ERR_HIP = 7,          /* a HIP launch failed (asynchronous faults surface at the caller's next sync) */
     KD_ERR_INTERNAL = 8
 } kd_status;

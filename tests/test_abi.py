@@ -60,6 +60,8 @@ def ws_size(lib, p, op):
     (dict(tau=0.0), B.KD_ERR_VALUE), (dict(tau=-1.0), B.KD_ERR_VALUE), (dict(tau=float("nan")), B.KD_ERR_VALUE),
     (dict(tau=float("inf")), B.KD_ERR_VALUE), (dict(dtype=7), B.KD_ERR_UNSUPPORTED),
     (dict(d=60), B.KD_ERR_UNSUPPORTED), (dict(K=1025, V=5000), B.KD_ERR_UNSUPPORTED),
+    (dict(V=(1 << 21) + 1), B.KD_ERR_UNSUPPORTED), (dict(T=1 << 31), B.KD_ERR_UNSUPPORTED),
+    (dict(chunk=(1 << 20) + 1), B.KD_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(lib, kw, status):
     st, _ = ws_size(lib, prob(**kw), B.KD_OP_FUSED)
