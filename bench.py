@@ -112,7 +112,7 @@ def bench_select(args) -> int:
     ev.rt.hipEventRecord(ctypes.c_void_p(whole[1]), ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     ms = ev.elapsed_ms(whole[0], whole[1]) / args.steps
-    ev.destroy(whole)
+    ev.destroy(marks)
     algo_bytes = T * V * 2 + T * K * 8           # read the logits once, write ids + fp32 logits
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     out = {
@@ -228,22 +228,24 @@ def main() -> int:
         cnt = ctypes.c_int(0)
         B._check("kd_topk_kl_set_stage_events", lib.kd_topk_kl_set_stage_events(st, b, e, cap, ctypes.byref(cnt)))
         tables.append((b, e, cnt))
-    whole = ev.create(2)
+    # one event before the first timed step and one after each step
+    marks = ev.create(args.steps + 1)
     stream = torch.cuda.current_stream()
     torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev.rt.hipEventRecord(ctypes.c_void_p(whole[0]), ctypes.c_void_p(stream.cuda_stream))
-    for _ in range(args.steps):
+    ev.rt.hipEventRecord(ctypes.c_void_p(marks[0]), ctypes.c_void_p(stream.cuda_stream))
+    for i in range(args.steps):
         step()
-    ev.rt.hipEventRecord(ctypes.c_void_p(whole[1]), ctypes.c_void_p(stream.cuda_stream))
+        ev.rt.hipEventRecord(ctypes.c_void_p(marks[i + 1]), ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for st in range(4):
         lib.kd_topk_kl_set_stage_events(st, None, None, 0, None)
     peak_gib = torch.cuda.max_memory_allocated() / 2**30
-    gpu_ms = ev.elapsed_ms(whole[0], whole[1])
+    gpu_ms = ev.elapsed_ms(marks[0], marks[args.steps])
     ms_per_step = gpu_ms / args.steps
+    step_ms = sorted(ev.elapsed_ms(marks[i], marks[i + 1]) for i in range(args.steps))
 
     # per-stage durations
     stages = {}
@@ -255,7 +257,7 @@ def main() -> int:
                                          total_ms_per_step=sum(durs) / args.steps)
         ev.destroy(b)
         ev.destroy(e)
-    ev.destroy(whole)
+    ev.destroy(marks)
     dom = max(stages, key=lambda k: stages[k]["total_ms_per_step"])
     flops_step = 6.0 * T * d * V
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
@@ -292,6 +294,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 3),
+        "ms_per_step_min": round(step_ms[0], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
