@@ -81,9 +81,15 @@ def cpu_baseline(x, rows: int) -> dict:
     t0 = time.perf_counter()
     kd_oracle.full(x.H[sel], x.W, x.topk_idx[sel], x.topk_logit[sel], x.ignore[sel], tau=x.tau)
     dt = time.perf_counter() - t0
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": rows / dt, "unit": "tokens/s", "cores": kd_oracle.num_threads(), "kind": "oracle",
             "sample": f"first {rows} positions of the workload, full vocabulary, fwd + grad_H + grad_W, "
-                      f"fp64, {dt:.1f} s"}
+                      f"fp64, {dt:.1f} s", "cpu": cpu}
 
 
 def bench_select(args) -> int:
@@ -112,7 +118,7 @@ def bench_select(args) -> int:
     ev.rt.hipEventRecord(ctypes.c_void_p(whole[1]), ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     ms = ev.elapsed_ms(whole[0], whole[1]) / args.steps
-    ev.destroy(marks)
+    ev.destroy(whole)
     algo_bytes = T * V * 2 + T * K * 8           # read the logits once, write ids + fp32 logits
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     out = {
