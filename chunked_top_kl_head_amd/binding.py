@@ -34,6 +34,8 @@ EXPORTS = (
     "kd_topk_kl_set_stage_events",
     "kd_status_string",
     "kd_topk_select",
+    "kd_teacher_topk_workspace_size",
+    "kd_teacher_topk",
 )
 KD_STAGE_LOGITS, KD_STAGE_ROWS, KD_STAGE_GRAD_H, KD_STAGE_GRAD_W = 0, 1, 2, 3
 STAGE_NAMES = ("logits", "rows", "grad_H", "grad_W")
@@ -48,6 +50,11 @@ class KdProblem(ctypes.Structure):
 class KdSelectProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int64), ("ld", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class KdTeacherProblem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("V", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class KdError(RuntimeError):
@@ -88,6 +95,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kd_topk_kl_set_stage_events.restype = ctypes.c_int
     lib.kd_topk_select.argtypes = [ctypes.POINTER(KdSelectProblem), vp, vp, vp, vp]
     lib.kd_topk_select.restype = ctypes.c_int
+    lib.kd_teacher_topk_workspace_size.argtypes = [ctypes.POINTER(KdTeacherProblem), ctypes.POINTER(sz)]
+    lib.kd_teacher_topk_workspace_size.restype = ctypes.c_int
+    lib.kd_teacher_topk.argtypes = [ctypes.POINTER(KdTeacherProblem), vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_teacher_topk.restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -262,4 +273,37 @@ def kd_topk_select(logits, K: int, V: Optional[int] = None, stream=None):
     val = torch.empty((T, K), dtype=torch.float32, device=logits.device)
     st = load_library().kd_topk_select(ctypes.byref(prob), _ptr(logits), _ptr(idx), _ptr(val), _stream(stream))
     _check("kd_topk_select", st)
+    return idx, val
+
+
+def kd_teacher_topk(H, W, K: int, chunk: int = 0, workspace=None, stream=None):
+    """The teacher cache from hidden states H [T, d] and the lm_head W [V, d] (bf16 or fp32, device):
+    per position the K largest logits H W^T and their ids, descending, equal values by id.
+    Returns (topk_idx int32 [T, K], topk_logit fp32 [T, K])."""
+    if not (H.is_cuda and W.is_cuda) or H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("H [T, d] and W [V, d] must be device tensors with the same d")
+    if H.dtype != W.dtype:
+        raise ValueError("H and W must have the same dtype")
+    if H.dtype == torch.bfloat16:
+        dt = KD_BF16
+    elif H.dtype == torch.float32:
+        dt = KD_F32
+    else:
+        raise ValueError(f"unsupported dtype {H.dtype}")
+    H, W = H.contiguous(), W.contiguous()
+    T, d = H.shape
+    V = W.shape[0]
+    prob = KdTeacherProblem(int(T), int(d), int(V), int(K), int(chunk), dt, 0)
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check("kd_teacher_topk_workspace_size", lib.kd_teacher_topk_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=H.device)
+    elif workspace.numel() * workspace.element_size() < n.value:
+        raise ValueError("workspace too small")
+    idx = torch.empty((T, K), dtype=torch.int32, device=H.device)
+    val = torch.empty((T, K), dtype=torch.float32, device=H.device)
+    st = lib.kd_teacher_topk(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(idx), _ptr(val), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("kd_teacher_topk", st)
     return idx, val

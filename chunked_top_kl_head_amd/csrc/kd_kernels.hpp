@@ -243,6 +243,47 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
 };
 
 // ---------------------------------------------------------------------------
+// Raw logit epilogue (teacher cache producer): the tile Z^T (rows = vocabulary
+// ids v, columns = chunk rows t) is stored as fp32 into out[t * ld + v] for
+// v < V and t < rows, four consecutive ids (16 bytes) per store; ld is a
+// multiple of 4 and out 16-byte aligned.
+// ---------------------------------------------------------------------------
+struct RawLogitsParams {
+    float* out;
+    int64_t ld;
+    int V, rows;
+};
+
+template <typename E, int BM, int BN> struct RawLogitsEpi {
+    using Params = RawLogitsParams;
+    template <class Mma>
+    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int,
+                                                 lds_t*, const Params& p) {
+        constexpr int FM = Mma::FM, FN = Mma::FN;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int t = n0 + Mma::col(wn, j, lane);
+            if (t >= p.rows) continue;
+            float* row = p.out + (int64_t)t * p.ld;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int v0 = m0 + Mma::row(wm, i, q, lane);   // multiple of 4
+                    if (v0 + 3 < p.V) {
+                        *reinterpret_cast<f32x4*>(row + v0) = f32x4{mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1],
+                                                                     mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]};
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (v0 + r < p.V) row[v0 + r] = mma.acc[i][j][4 * q + r];
+                    }
+                }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // grad_H epilogue: tile of dH^T (rows = hidden index j, columns = chunk rows t).
 // One split writes grad_H directly; several splits write fp32 partials that a
 // fixed-order reduction sums.

@@ -374,6 +374,55 @@ static kd_status dispatch(const Plan& pl, int dtype, kd_op op, const void* H, co
                       ws, s);
 }
 
+// Teacher cache from hidden states: per chunk, the logits GEMM writes the
+// chunk's fp32 logits [rows][ld] into the workspace and the select kernel
+// reduces each row.
+struct TeacherPlan {
+    int64_t T, d, V, K, C, V_pad, ld;
+    int es;
+    size_t total;
+};
+
+static kd_status teacher_plan(const kd_teacher_problem* p, TeacherPlan* out) {
+    if (!p) return KD_ERR_NULL;
+    if (p->T < 0 || p->d < 1 || p->V < 1 || p->K < 1 || p->K > p->V || p->chunk < 0) return KD_ERR_SHAPE;
+    if (p->reserved != 0) return KD_ERR_VALUE;
+    if (p->dtype != KD_BF16 && p->dtype != KD_F32) return KD_ERR_UNSUPPORTED;
+    if (p->d % 8 != 0 || p->K > kSelMaxK || p->V > ((int64_t)1 << 21) || p->T > 0x7FFFFFFFLL || p->d > (1 << 20) ||
+        p->chunk > (1 << 20))
+        return KD_ERR_UNSUPPORTED;
+    TeacherPlan q{};
+    q.T = p->T; q.d = p->d; q.V = p->V; q.K = p->K;
+    q.es = p->dtype == KD_BF16 ? 2 : 4;
+    q.C = p->chunk > 0 ? p->chunk : 4096;
+    q.V_pad = cdiv(q.V, BM) * BM;
+    q.ld = cdiv(q.V, 4) * 4;
+    if (q.es == 4 && ((q.V_pad + BM) * q.d * q.es >= kOperandLimit || (q.C + BN) * q.d * q.es >= kOperandLimit))
+        return KD_ERR_UNSUPPORTED;
+    q.total = align256((size_t)(q.C * q.ld) * sizeof(float));
+    *out = q;
+    return KD_OK;
+}
+
+template <typename E>
+static kd_status run_teacher(const TeacherPlan& pl, const void* H, const void* W, int32_t* idx, float* val, void* ws,
+                             hipStream_t stream) {
+    float* z = static_cast<float*>(ws);
+    const int bk = 128 / pl.es;
+    for (int64_t t0 = 0; t0 < pl.T; t0 += pl.C) {
+        const int64_t rc = pl.T - t0 < pl.C ? pl.T - t0 : pl.C;
+        const Operand A = operand(W, pl.d, pl.V * pl.d * pl.es);
+        const Operand B = operand(static_cast<const char*>(H) + t0 * pl.d * pl.es, pl.d, rc * pl.d * pl.es);
+        const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk);
+        RawLogitsParams rp{};
+        rp.out = z; rp.ld = pl.ld; rp.V = (int)pl.V; rp.rows = (int)rc;
+        launch_gemm<E, true, true, false, RawLogitsEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, rp);
+        hipLaunchKernelGGL(topk_select_kernel<float>, dim3((unsigned)rc), dim3(kSelThreads), 0, stream, z, pl.ld,
+                           (int)pl.V, (int)pl.K, idx + t0 * pl.K, val + t0 * pl.K);
+    }
+    return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
+}
+
 }  // namespace kd
 
 using namespace kd;
@@ -542,6 +591,40 @@ kd_status kd_topk_select(const kd_select_problem* prob, const void* logits, int3
             hipLaunchKernelGGL(topk_select_kernel<float>, dim3((unsigned)p.T), dim3(kSelThreads), 0, s, logits, p.ld,
                                (int)p.V, (int)p.K, topk_idx, topk_logit);
         return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_teacher_topk_workspace_size(const kd_teacher_problem* prob, size_t* bytes) {
+    try {
+        if (!bytes) return KD_ERR_NULL;
+        TeacherPlan pl;
+        const kd_status st = teacher_plan(prob, &pl);
+        if (st != KD_OK) return st;
+        *bytes = pl.total;
+        return KD_OK;
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_teacher_topk(const kd_teacher_problem* prob, const void* H, const void* W, int32_t* topk_idx,
+                          float* topk_logit, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        TeacherPlan pl;
+        const kd_status st = teacher_plan(prob, &pl);
+        if (st != KD_OK) return st;
+        if (pl.T == 0) return KD_OK;
+        if (!H || !W || !topk_idx || !topk_logit || !workspace) return KD_ERR_NULL;
+        if (!aligned(H, 16) || !aligned(W, 16) || !aligned(workspace, 16) || !aligned(topk_idx, 4) ||
+            !aligned(topk_logit, 4))
+            return KD_ERR_ALIGN;
+        if (workspace_bytes < pl.total) return KD_ERR_WORKSPACE;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        (void)hipGetLastError();
+        if (pl.es == 2) return run_teacher<bf16_t>(pl, H, W, topk_idx, topk_logit, workspace, s);
+        return run_teacher<float>(pl, H, W, topk_idx, topk_logit, workspace, s);
     } catch (...) {
         return KD_ERR_INTERNAL;
     }

@@ -52,6 +52,38 @@ typedef struct {
 kd_status kd_topk_select(const kd_select_problem* prob, const void* logits, int32_t* topk_idx, float* topk_logit,
                          void* stream);
 
+/*
+ * Teacher cache straight from the teacher's last hidden states: for every
+ * position t, the K largest of the logits z[t, v] = H[t, :] . W[v, :] over the
+ * whole vocabulary, with their ids, in the order of kd_topk_select (the same
+ * source passage: the teacher runs once and only its top-K logits per position
+ * are kept).  The logits are computed with fp32 accumulation of the operand
+ * dtype, chunk by chunk (`chunk` positions at a time, 0 = 4096): each chunk's
+ * fp32 logits go to the workspace and are reduced there, so the [T, V] logit
+ * matrix never exists and the workspace does not depend on T.
+ *
+ * Layouts: H [T, d] and W [V, d] row-major (the nn.Linear weight layout), bf16
+ * or fp32, 16-byte aligned, d a multiple of 8; topk_idx [T, K] int32 and
+ * topk_logit [T, K] fp32, 4-byte aligned; workspace 16-byte aligned, at least
+ * kd_teacher_topk_workspace_size bytes.  Ownership, streams and the error
+ * convention as above; KD_ERR_UNSUPPORTED also for d % 8 != 0, V > 2^21,
+ * chunk > 2^20, or (fp32) an operand beyond 2^31 bytes; KD_ERR_WORKSPACE when
+ * workspace_bytes is too small.
+ */
+typedef struct {
+    int64_t T;          /* positions */
+    int64_t d;          /* hidden size */
+    int64_t V;          /* vocabulary size */
+    int64_t K;          /* kept per position, 1 <= K <= min(V, 1024) */
+    int64_t chunk;      /* positions per chunk, 0 = default */
+    int32_t dtype;      /* kd_dtype of H and W */
+    int32_t reserved;   /* must be 0 */
+} kd_teacher_problem;
+
+kd_status kd_teacher_topk_workspace_size(const kd_teacher_problem* prob, size_t* bytes);
+kd_status kd_teacher_topk(const kd_teacher_problem* prob, const void* H, const void* W, int32_t* topk_idx,
+                          float* topk_logit, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -251,3 +251,57 @@ def test_select_argument_errors(lib):
     assert lib.kd_topk_select(ctypes.byref(p), P16, P4, MIS, None) == B.KD_ERR_ALIGN
     # no rows: nothing to do, nothing dereferenced
     assert lib.kd_topk_select(ctypes.byref(sel(T=0)), None, None, None, None) == B.KD_OK
+
+
+def teacher(T=64, d=64, V=1000, K=10, chunk=0, dtype=B.KD_BF16, reserved=0):
+    return B.KdTeacherProblem(T, d, V, K, chunk, dtype, reserved)
+
+
+def teacher_ws(lib, p):
+    n = ctypes.c_size_t(0)
+    return lib.kd_teacher_topk_workspace_size(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+def test_teacher_struct_layout():
+    assert ctypes.sizeof(B.KdTeacherProblem) == 48
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), B.KD_ERR_SHAPE), (dict(d=0), B.KD_ERR_SHAPE), (dict(V=0), B.KD_ERR_SHAPE),
+    (dict(K=0), B.KD_ERR_SHAPE), (dict(K=1001), B.KD_ERR_SHAPE), (dict(chunk=-1), B.KD_ERR_SHAPE),
+    (dict(reserved=1), B.KD_ERR_VALUE), (dict(dtype=9), B.KD_ERR_UNSUPPORTED), (dict(d=60), B.KD_ERR_UNSUPPORTED),
+    (dict(V=5000, K=1025), B.KD_ERR_UNSUPPORTED), (dict(V=(1 << 21) + 1), B.KD_ERR_UNSUPPORTED),
+    (dict(T=1 << 31), B.KD_ERR_UNSUPPORTED), (dict(chunk=(1 << 20) + 1), B.KD_ERR_UNSUPPORTED),
+    (dict(d=8192, V=200000, dtype=B.KD_F32), B.KD_ERR_UNSUPPORTED),
+])
+def test_teacher_validation(lib, kw, status):
+    assert teacher_ws(lib, teacher(**kw))[0] == status
+    assert lib.kd_teacher_topk(ctypes.byref(teacher(**kw)), P16, P16b, P4, P4, P16, 1 << 40, None) == status
+
+
+def test_teacher_workspace_independent_of_T(lib):
+    # one chunk of fp32 logits, rows padded to a multiple of 4 values
+    st1, n1 = teacher_ws(lib, teacher(T=10, V=1001, chunk=512))
+    st2, n2 = teacher_ws(lib, teacher(T=100000, V=1001, chunk=512))
+    assert st1 == st2 == B.KD_OK and n1 == n2 and n1 >= 512 * 1004 * 4
+    assert teacher_ws(lib, teacher(V=1001))[1] >= 4096 * 1004 * 4   # default chunk 4096
+
+
+def test_teacher_argument_errors(lib):
+    p = teacher()
+    st, n = teacher_ws(lib, p)
+    assert st == B.KD_OK
+    assert lib.kd_teacher_topk_workspace_size(ctypes.byref(p), None) == B.KD_ERR_NULL
+    assert lib.kd_teacher_topk(None, P16, P16b, P4, P4, P16, n, None) == B.KD_ERR_NULL
+    assert lib.kd_teacher_topk(ctypes.byref(p), None, P16b, P4, P4, P16, n, None) == B.KD_ERR_NULL
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, None, P4, P4, P16, n, None) == B.KD_ERR_NULL
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, P16b, None, P4, P16, n, None) == B.KD_ERR_NULL
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, P16b, P4, None, P16, n, None) == B.KD_ERR_NULL
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, P16b, P4, P4, None, n, None) == B.KD_ERR_NULL
+    assert lib.kd_teacher_topk(ctypes.byref(p), MIS, P16b, P4, P4, P16, n, None) == B.KD_ERR_ALIGN
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, MIS, P4, P4, P16, n, None) == B.KD_ERR_ALIGN
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, P16b, MIS, P4, P16, n, None) == B.KD_ERR_ALIGN
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, P16b, P4, P4, P4, n, None) == B.KD_ERR_ALIGN
+    assert lib.kd_teacher_topk(ctypes.byref(p), P16, P16b, P4, P4, P16, n - 1, None) == B.KD_ERR_WORKSPACE
+    # no positions: nothing to do, nothing dereferenced
+    assert lib.kd_teacher_topk(ctypes.byref(teacher(T=0)), None, None, None, None, None, 0, None) == B.KD_OK

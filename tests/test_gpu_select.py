@@ -94,3 +94,70 @@ def test_full_size_teacher_cache():
     assert np.array_equal(idx[torch.from_numpy(rows).cuda()].cpu().numpy(), ref_idx)
     assert np.array_equal(val[torch.from_numpy(rows).cuda()].cpu().numpy(), ref_val)
     say(f"  {rows.size} sampled rows exact; all {T} rows ordered")
+
+
+# ---------------------------------------------------------------------------
+# kd_teacher_topk: the cache straight from the teacher's hidden states.  The
+# logits are fp32 sums of d products, so near-ties at the K-th value may be
+# ordered either way: what is unique is checked exactly (every id far enough
+# above the K-th logit is kept, nothing far below it is), the rest for
+# validity (distinct ids in range, values = the logits at the ids within the
+# fp32 summation bound, descending).
+# ---------------------------------------------------------------------------
+def check_teacher(H64, W64, idx, val, K):
+    d = H64.shape[1]
+    z = H64 @ W64.T
+    bound = (np.abs(H64) @ np.abs(W64).T) * (d * 2.0 ** -24) + 1e-30
+    T, V = z.shape
+    assert idx.shape == (T, K) and val.shape == (T, K)
+    for t in range(T):
+        ids = idx[t].astype(np.int64)
+        assert np.all((ids >= 0) & (ids < V)) and np.unique(ids).size == K
+        assert np.all(np.abs(val[t].astype(np.float64) - z[t, ids]) <= bound[t, ids])
+        assert np.all(val[t, :-1] >= val[t, 1:])
+        zK = np.partition(z[t], V - K)[V - K]          # K-th largest logit
+        margin = 2.0 * bound[t].max()
+        assert np.all(z[t, ids] >= zK - margin)
+        must = np.nonzero(z[t] > zK + margin)[0]
+        assert np.isin(must, ids).all()
+
+
+@pytest.mark.parametrize("dtype,T,d,V,K,chunk", [
+    ("bf16", 300, 256, 5000, 20, 128),     # three chunks, the last ragged; vocabulary tail in the last tile
+    ("bf16", 70, 136, 3001, 100, 0),       # V not a multiple of 4 (padded rows of the chunk buffer)
+    ("bf16", 33, 64, 37, 37, 16),          # K = V
+    ("f32", 100, 64, 1000, 10, 64),
+])
+def test_teacher_topk(dtype, T, d, V, K, chunk):
+    from chunked_top_kl_head_amd import synth
+    x = synth.make_inputs(T, d, V, K, tau=1.0, dtype=dtype, seed=31, mask=None)
+    if dtype == "bf16":
+        H = torch.from_numpy(x.H_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        W = torch.from_numpy(x.W_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        H = torch.from_numpy(x.H).cuda()
+        W = torch.from_numpy(x.W).cuda()
+    idx, val = B.kd_teacher_topk(H, W, K, chunk=chunk)
+    torch.cuda.synchronize()
+    check_teacher(x.H.astype(np.float64), x.W.astype(np.float64), idx.cpu().numpy(), val.cpu().numpy(), K)
+    say(f"  teacher top-{K}: {dtype} T={T} d={d} V={V} chunk={chunk} ok")
+
+
+def test_teacher_topk_full_size():
+    """GPT-OSS-like teacher shapes (T = 32,768, d = 2,880, V = 201,088, K = 100,
+    bf16): every row ordered with distinct ids; 24 sampled rows against the
+    fp64 oracle."""
+    from chunked_top_kl_head_amd import synth
+    x = synth.workload_inputs("gptoss20b")
+    H = torch.from_numpy(x.H_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    W = torch.from_numpy(x.W_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    K = 100
+    idx, val = B.kd_teacher_topk(H, W, K)
+    torch.cuda.synchronize()
+    assert bool((val[:, 1:] <= val[:, :-1]).all())
+    s, _ = torch.sort(idx, dim=1)
+    assert bool((s[:, 1:] != s[:, :-1]).all()) and int(idx.min()) >= 0 and int(idx.max()) < x.V
+    rows = np.unique(np.concatenate([[0, x.T - 1], np.random.default_rng(3).choice(x.T, 22, replace=False)]))
+    r = torch.from_numpy(rows).cuda()
+    check_teacher(x.H[rows].astype(np.float64), x.W.astype(np.float64), idx[r].cpu().numpy(), val[r].cpu().numpy(), K)
+    say(f"  {rows.size} sampled rows valid; all {x.T} rows ordered")
