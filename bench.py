@@ -145,6 +145,62 @@ def bench_select(args) -> int:
     return 0
 
 
+def bench_teacher(args) -> int:
+    """The cache producer from hidden states (kd_teacher_topk) with the
+    workload's H [T, d] and W [V, d] standing in for the teacher's: per chunk a
+    logits GEMM into fp32 and the per-row top-K.  One step = one call over all
+    positions; prints one JSON line (dominant cost: the GEMM, 2 T d V FLOP)."""
+    import numpy as np
+    import torch
+
+    from chunked_top_kl_head_amd import binding as B
+    from chunked_top_kl_head_amd import synth
+
+    x = synth.workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    if x.dtype == "bf16":
+        H = torch.from_numpy(x.H_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(x.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        H = torch.from_numpy(x.H).to(dev)
+        W = torch.from_numpy(x.W).to(dev)
+    T, d, V, K = x.T, x.d, x.V, 100
+    chunk = args.chunk or 4096
+    prob = B.KdTeacherProblem(T, d, V, K, chunk, B.KD_BF16 if x.dtype == "bf16" else B.KD_F32, 0)
+    lib = B.load_library()
+    n = ctypes.c_size_t(0)
+    B._check("kd_teacher_topk_workspace_size", lib.kd_teacher_topk_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    ws = torch.empty(int(n.value), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        B.kd_teacher_topk(H, W, K, chunk=chunk, workspace=ws)
+    ev = HipEvents()
+    whole = ev.create(2)
+    stream = torch.cuda.current_stream()
+    torch.cuda.reset_peak_memory_stats()
+    torch.cuda.synchronize()
+    ev.rt.hipEventRecord(ctypes.c_void_p(whole[0]), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        B.kd_teacher_topk(H, W, K, chunk=chunk, workspace=ws)
+    ev.rt.hipEventRecord(ctypes.c_void_p(whole[1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(whole[0], whole[1]) / args.steps
+    ev.destroy(whole)
+    tflops = 2.0 * T * d * V / (ms * 1e-3) / 1e12
+    peak = 2500.0 if x.dtype == "bf16" else 157.3
+    out = {
+        "metric": "teacher top-K cache rows/s from hidden states (top-100 of H W^T per position)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": x.dtype, "data": "synthetic (seeded H, W)",
+        "config": {"workload": f"teacher_topk: T={T} d={d} V={V} K={K} {x.dtype}", "chunk": chunk},
+        "tflops": round(tflops, 2), "peak_hbm_gib": round(torch.cuda.max_memory_allocated() / 2**30, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None, "kernel": "whole call"},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     from chunked_top_kl_head_amd import synth
 
@@ -160,6 +216,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--select", action="store_true",
                     help="benchmark the teacher top-K cache producer instead of the loss")
+    ap.add_argument("--teacher", action="store_true",
+                    help="benchmark the cache producer from hidden states (kd_teacher_topk): the workload's "
+                         "H and W as the teacher's, K = 100")
     ap.add_argument("--copy-calibration-bytes", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many bytes (a kernel of known "
                          "traffic, used to scale the FETCH_SIZE/WRITE_SIZE counters of a profiling run)")
@@ -181,6 +240,8 @@ def main() -> int:
         return 1
     if args.select:
         return bench_select(args)
+    if args.teacher:
+        return bench_teacher(args)
     wl = synth.WORKLOADS[args.workload]
     chunk = args.chunk or wl.chunk
     t_gen = time.perf_counter()
