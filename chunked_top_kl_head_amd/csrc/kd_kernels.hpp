@@ -245,8 +245,7 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
 // ---------------------------------------------------------------------------
 // Raw logit epilogue (teacher cache producer): the tile Z^T (rows = vocabulary
 // ids v, columns = chunk rows t) is stored as fp32 into out[t * ld + v] for
-// v < V and t < rows, four consecutive ids (16 bytes) per store; ld is a
-// multiple of 4 and out 16-byte aligned.
+// v < V and t < rows; ld is a multiple of 4 and out 16-byte aligned.
 // ---------------------------------------------------------------------------
 struct RawLogitsParams {
     float* out;
@@ -256,29 +255,81 @@ struct RawLogitsParams {
 
 template <typename E, int BM, int BN> struct RawLogitsEpi {
     using Params = RawLogitsParams;
+    static constexpr bool kStaged = Elem<E>::size == 2;   // bf16 engine: stage LDS free for the epilogue
+
     template <class Mma>
-    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int,
-                                                 lds_t*, const Params& p) {
+    static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int tid,
+                                                 lds_t* smem, const Params& p) {
         constexpr int FM = Mma::FM, FN = Mma::FN;
+        if constexpr (kStaged) {
+            // Two passes over halves of 128 vocabulary ids (held by the waves
+            // with wm = half): the half tile goes to LDS as [t][128] fp32
+            // (16-byte chunk c of row t at slot c ^ (t & 31)), then every wave
+            // writes whole 512-byte row segments of the output.
+            const int wave = tid >> 6;
+            const int c = lane & 31;
+            constexpr int RW = 256 / kDtlWaves;   // staged rows per wave
+            __syncthreads();   // every wave is past its main loop: the stage LDS is free
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int t = n0 + Mma::col(wn, j, lane);
-            if (t >= p.rows) continue;
-            float* row = p.out + (int64_t)t * p.ld;
+            for (int half = 0; half < 2; ++half) {
+                if (wm == half) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                    for (int j = 0; j < FN; ++j) {
+                        const int t = Mma::col(wn, j, lane);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int v0 = m0 + Mma::row(wm, i, q, lane);   // multiple of 4
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int vv = Mma::row(0, i, q, lane);   // within the half, multiple of 4
+                                *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(
+                                    smem + t * 512 + (((vv >> 2) ^ (t & 31)) << 4)) =
+                                    f32x4{mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
+                                          mma.acc[i][j][4 * q + 3]};
+                            }
+                    }
+                }
+                __syncthreads();
+                const int v0 = m0 + 128 * half + 4 * c;
+#pragma unroll
+                for (int k = 0; k < RW / 2; ++k) {
+                    const int tl = wave * RW + 2 * k + (lane >> 5);
+                    const f32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                        smem + tl * 512 + ((c ^ (tl & 31)) << 4));
+                    const int t = n0 + tl;
+                    if (t >= p.rows) continue;
+                    float* dst = p.out + (int64_t)t * p.ld + v0;
                     if (v0 + 3 < p.V) {
-                        *reinterpret_cast<f32x4*>(row + v0) = f32x4{mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1],
-                                                                     mma.acc[i][j][4 * q + 2], mma.acc[i][j][4 * q + 3]};
+                        *reinterpret_cast<f32x4*>(dst) = val;
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            if (v0 + r < p.V) row[v0 + r] = mma.acc[i][j][4 * q + r];
+                            if (v0 + r < p.V) dst[r] = val[r];
                     }
                 }
+                if (half == 0) __syncthreads();
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int t = n0 + Mma::col(wn, j, lane);
+                if (t >= p.rows) continue;
+                float* row = p.out + (int64_t)t * p.ld;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int v0 = m0 + Mma::row(wm, i, q, lane);   // multiple of 4
+                        if (v0 + 3 < p.V) {
+                            *reinterpret_cast<f32x4*>(row + v0) =
+                                f32x4{mma.acc[i][j][4 * q], mma.acc[i][j][4 * q + 1], mma.acc[i][j][4 * q + 2],
+                                      mma.acc[i][j][4 * q + 3]};
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (v0 + r < p.V) row[v0 + r] = mma.acc[i][j][4 * q + r];
+                        }
+                    }
+            }
         }
     }
 };
