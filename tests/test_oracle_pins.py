@@ -28,6 +28,19 @@ from chunked_top_kl_head_amd.synth import make_inputs
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
 
 
+@pytest.fixture(scope="module", params=["c_loops", "matrix_products"])
+def oracle(request):
+    """Every pin holds for both writings of the definition: the plain C loops
+    (oracle/kd_oracle.c) and the numpy version whose contractions are library
+    matrix products (oracle/kd_oracle_blas.py, used at full-vocabulary sizes)."""
+    if request.param == "c_loops":
+        from oracle import kd_oracle
+        kd_oracle._load()
+        return kd_oracle
+    from oracle import kd_oracle_blas
+    return kd_oracle_blas
+
+
 def _rel(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -298,3 +311,22 @@ def test_gradient_identities(oracle):
     lhs = float((gw * x.W.astype(np.float64)).sum())
     rhs = float((gh * x.H.astype(np.float64)).sum())
     assert abs(lhs - rhs) <= 1e-12 * max(abs(lhs), 1e-30)
+
+
+def test_two_oracles_agree():
+    """The C loops and the matrix-product version agree on a problem with bf16
+    operands, ignored rows, duplicate ids, -inf teacher logits, tau = 2 and a
+    ragged last chunk, also when only some grad_W rows are requested."""
+    from oracle import kd_oracle, kd_oracle_blas
+    x = make_inputs(90, 40, 700, 24, tau=2.0, dtype="bf16", seed=91, mask=("random", 0.2), w_std=0.3)
+    x.topk_idx[:, 7] = x.topk_idx[:, 3]
+    x.topk_logit[5, 10:] = -np.inf
+    a = kd_oracle.full(x.H, x.W, x.topk_idx, x.topk_logit, x.ignore, tau=2.0, g=0.5, chunk=32)
+    b = kd_oracle_blas.full(x.H, x.W, x.topk_idx, x.topk_logit, x.ignore, tau=2.0, g=0.5, chunk=32)
+    assert abs(a["loss"] - b["loss"]) <= 1e-13 * abs(a["loss"])
+    for k in ("lse", "row_loss", "grad_H", "grad_W"):
+        assert _rel(b[k], a[k]) <= 1e-13, k
+    sel = np.array([0, 5, int(x.topk_idx[0, 0]), 699])
+    c = kd_oracle_blas.full(x.H, x.W, x.topk_idx, x.topk_logit, x.ignore, tau=2.0, g=0.5, chunk=64, w_rows=sel)
+    assert _rel(c["grad_W_rows"], a["grad_W"][sel]) <= 1e-13
+    np.testing.assert_allclose(c["lse"], a["lse"], rtol=1e-14)
