@@ -287,10 +287,16 @@ def main() -> int:
     lib = B.load_library()
     ev = HipEvents()
     nchunks = (T + chunk - 1) // chunk
-    passes = 2 if args.mode == "split" else 1     # logits and rows run in both forward and backward
-    cap = args.steps * nchunks * passes
+    # launches per chunk and stage: the row kernel runs before and after the
+    # logits GEMM in the forward and fused entries and once more in the split
+    # backward; the split path runs the logits GEMM in both passes
+    split = args.mode == "split"
+    per_chunk = {B.KD_STAGE_LOGITS: 2 if split else 1, B.KD_STAGE_ROWS: 3 if split else 2,
+                 B.KD_STAGE_GRAD_H: 1, B.KD_STAGE_GRAD_W: 1}
+    expected = {st: args.steps * nchunks * n for st, n in per_chunk.items()}
     tables = []
     for st in range(4):
+        cap = expected[st]
         b, e = ev.create(cap), ev.create(cap)
         cnt = ctypes.c_int(0)
         B._check("kd_topk_kl_set_stage_events", lib.kd_topk_kl_set_stage_events(st, b, e, cap, ctypes.byref(cnt)))
@@ -319,6 +325,8 @@ def main() -> int:
     rows_full = min(chunk, T)
     for st, (b, e, cnt) in enumerate(tables):
         n = cnt.value
+        if n != expected[st]:
+            raise RuntimeError(f"stage {B.STAGE_NAMES[st]}: {n} launches recorded, {expected[st]} expected")
         durs = [ev.elapsed_ms(b[i], e[i]) for i in range(n)]
         stages[B.STAGE_NAMES[st]] = dict(launches=n, avg_ms=(sum(durs) / n if n else 0.0),
                                          total_ms_per_step=sum(durs) / args.steps)

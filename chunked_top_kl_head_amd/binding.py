@@ -89,7 +89,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kd_topk_kl_fused.restype = ctypes.c_int
     lib.kd_topk_kl_validate.argtypes = [prob, vp, vp, vp, vp, vp]
     lib.kd_topk_kl_validate.restype = ctypes.c_int
-    lib.kd_topk_kl_scale_grads.argtypes = [prob, vp, vp, vp, vp]
+    lib.kd_topk_kl_scale_grads.argtypes = [prob, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
     lib.kd_topk_kl_scale_grads.restype = ctypes.c_int
     lib.kd_topk_kl_set_stage_events.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.kd_topk_kl_set_stage_events.restype = ctypes.c_int
@@ -239,20 +239,41 @@ def kd_topk_kl_validate(topk_idx, topk_logit, V, ignore=None, stream=None) -> to
     return bad
 
 
-def kd_topk_kl_scale_grads(grad_loss, grad_H=None, grad_W=None, stream=None):
-    """grad_H and grad_W (as returned by kd_topk_kl_fused) *= grad_loss[0], in place."""
-    ref = grad_H if grad_H is not None else grad_W
-    if ref is None:
-        return
+def kd_topk_kl_scale_grads(grad_loss=None, grad_H=None, grad_W=None, out_H=None, out_W=None, stream=None):
+    """out_H = g * grad_H and out_W = g * grad_W with g = grad_loss[0] (None: 1).
+
+    grad_H / grad_W as returned by kd_topk_kl_fused (grad_W fp32).  An output
+    left as None is the input itself (in place); out_W may be bfloat16 (the
+    scaled fp32 gradient rounded to nearest even).  Returns (out_H, out_W)."""
+    if grad_H is None and grad_W is None:
+        return None, None
+    if grad_H is not None and out_H is None:
+        out_H = grad_H
+    if grad_W is not None and out_W is None:
+        out_W = grad_W
+    for name, t in (("grad_H", grad_H), ("grad_W", grad_W), ("out_H", out_H), ("out_W", out_W)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if grad_W is not None and (grad_W.dtype != torch.float32 or out_W.shape != grad_W.shape):
+        raise ValueError("grad_W must be float32 and out_W of its shape")
+    if grad_H is not None and (out_H.dtype != grad_H.dtype or out_H.shape != grad_H.shape):
+        raise ValueError("out_H must match grad_H")
     T, d = (grad_H.shape if grad_H is not None else (0, grad_W.shape[1]))
     V = grad_W.shape[0] if grad_W is not None else 1
     dt = grad_H.dtype if grad_H is not None else torch.bfloat16
+    if out_W is None or out_W.dtype == torch.float32:
+        wdt = KD_F32
+    elif out_W.dtype == torch.bfloat16:
+        wdt = KD_BF16
+    else:
+        raise ValueError(f"unsupported out_W dtype {out_W.dtype}")
     prob = problem(T, d, V, 1, 1.0, dt, 0)
-    if grad_loss.dtype != torch.float32 or not grad_loss.is_cuda:
+    if grad_loss is not None and (grad_loss.dtype != torch.float32 or not grad_loss.is_cuda):
         raise ValueError("grad_loss must be a float32 device tensor")
     st = load_library().kd_topk_kl_scale_grads(ctypes.byref(prob), _ptr(grad_loss), _ptr(grad_H), _ptr(grad_W),
-                                               _stream(stream))
+                                               _ptr(out_H), _ptr(out_W), wdt, _stream(stream))
     _check("kd_topk_kl_scale_grads", st)
+    return out_H, out_W
 
 
 def kd_topk_select(logits, K: int, V: Optional[int] = None, stream=None):

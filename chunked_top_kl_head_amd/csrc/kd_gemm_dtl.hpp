@@ -71,7 +71,14 @@ __device__ __forceinline__ void dtl_load16(const u32x4& rsrc_in, uint32_t lds_ad
     // m0 is declared clobbered: the compiler keeps none of its own values in it
     // across the block (and saves it only where it has one).  An SALU write of
     // m0 needs one wait state before an LDS-DMA load reads it (the compiler pads
-    // its own such sequences with s_nop 0 on this target).
+    // its own such sequences with s_nop 0 on this target).  Clang warns that a
+    // reserved register in a clobber list may not be preserved; the kernels
+    // keep no value of their own in m0, which tests/test_static.py checks on
+    // the compiled device code (every m0 write is this block's, directly
+    // followed by its load, and nothing else reads m0), so only that warning
+    // is silenced, here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
@@ -79,6 +86,7 @@ __device__ __forceinline__ void dtl_load16(const u32x4& rsrc_in, uint32_t lds_ad
         :
         : "v"(voff), "s"(rsrc), "s"(lds_addr)
         : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 // Hides a per-lane value from loop-invariant code motion: the compiler would

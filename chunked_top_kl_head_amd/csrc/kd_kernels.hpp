@@ -167,13 +167,13 @@ template <typename E, int BM, int BN, int MODE> struct LogitsEpi {
             const float s = p.hdr->s;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const float st = kept[j] ? s : 0.f;
-                const float l2 = colv[j] * kLog2e;
+                // ignored (and padding) rows: exactly 0, whatever their lse
+                const float l2 = kept[j] ? colv[j] * kLog2e : INFINITY;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
-                        mma.acc[i][j][e] = st * fast_exp2(fmaf(mma.acc[i][j][e], sc, -l2));
+                        mma.acc[i][j][e] = s * fast_exp2(fmaf(mma.acc[i][j][e], sc, -l2));
             }
         } else {
             // this wave's 128 ids of each of its columns (lanes l and l + 32
@@ -696,7 +696,9 @@ __global__ __launch_bounds__(kThreads) void row_kernel(RowParams p) {
     if (two_pass && p.pre) {
         if (r == 0 && tid == 0) p.hdr->dirty = 0;
         if (!kept) {
-            if (tid == 0) p.ref[r] = 0.f;   // any finite reference: the row's G is multiplied by 0
+            // no reference: every block sums relative to its own max, so the
+            // row's lse stays finite however small its logits are (its G is 0)
+            if (tid == 0) p.ref[r] = -INFINITY;
             return;
         }
         for (int k = tid; k < K; k += kThreads) sh_id[k] = clamp_id(p.idx[(int64_t)t * K + k], p.V);
@@ -1027,21 +1029,38 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(const int32_t* idx, 
     }
 }
 
-// x *= g[0] over n16 16-byte chunks of element type E (bf16: rounded to nearest even).
-template <typename E>
-__global__ __launch_bounds__(kThreads) void scale_kernel(u32x4* x, int64_t n16, const float* g) {
-    const float s = *g;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kThreads) {
-        u32x4 v = x[i];
-        if constexpr (Elem<E>::size == 2) {
+// out = g[0] * in over n elements (g = NULL: 1), element types EI -> EO (bf16
+// results rounded to nearest even); n is a multiple of 8 (a whole 16-byte
+// chunk of bf16 input or output).  out may be in itself when EI == EO.
+template <typename EI, typename EO>
+__global__ __launch_bounds__(kThreads) void scale_kernel(const void* in, void* out, int64_t n, const float* g) {
+    const float s = g ? *g : 1.0f;
+    const int64_t n8 = n / 8;   // groups of 8 elements
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kThreads) {
+        float v[8];
+        if constexpr (Elem<EI>::size == 2) {
+            const u32x4 x = reinterpret_cast<const u32x4*>(in)[i];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                v[q] = pack_bf16x2(bf16_bits_to_f32(v[q] & 0xFFFFu) * s, bf16_bits_to_f32(v[q] >> 16) * s);
+            for (int q = 0; q < 4; ++q) {
+                v[2 * q] = bf16_bits_to_f32(x[q] & 0xFFFFu);
+                v[2 * q + 1] = bf16_bits_to_f32(x[q] >> 16);
+            }
         } else {
-            f32x4 f = __builtin_bit_cast(f32x4, v) * s;
-            v = __builtin_bit_cast(u32x4, f);
+            const f32x4 a = reinterpret_cast<const f32x4*>(in)[2 * i];
+            const f32x4 b = reinterpret_cast<const f32x4*>(in)[2 * i + 1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[q] = a[q];
+                v[4 + q] = b[q];
+            }
         }
-        x[i] = v;
+        if constexpr (Elem<EO>::size == 2) {
+            reinterpret_cast<u32x4*>(out)[i] = u32x4{pack_bf16x2(v[0] * s, v[1] * s), pack_bf16x2(v[2] * s, v[3] * s),
+                                                     pack_bf16x2(v[4] * s, v[5] * s), pack_bf16x2(v[6] * s, v[7] * s)};
+        } else {
+            reinterpret_cast<f32x4*>(out)[2 * i] = f32x4{v[0] * s, v[1] * s, v[2] * s, v[3] * s};
+            reinterpret_cast<f32x4*>(out)[2 * i + 1] = f32x4{v[4] * s, v[5] * s, v[6] * s, v[7] * s};
+        }
     }
 }
 

@@ -537,31 +537,46 @@ kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx, c
     }
 }
 
-kd_status kd_topk_kl_scale_grads(const kd_problem* prob, const float* grad_loss, void* grad_H, float* grad_W,
-                                 void* stream) {
+static inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+kd_status kd_topk_kl_scale_grads(const kd_problem* prob, const float* grad_loss, const void* grad_H,
+                                 const float* grad_W, void* out_H, void* out_W, int32_t out_w_dtype, void* stream) {
     try {
         kd_status st = check_problem(prob);
         if (st != KD_OK) return st;
-        if (!grad_loss) return KD_ERR_NULL;
-        if (!aligned(grad_loss, 4) || !aligned(grad_H, 16) || !aligned(grad_W, 16)) return KD_ERR_ALIGN;
+        if ((grad_H == nullptr) != (out_H == nullptr) || (grad_W == nullptr) != (out_W == nullptr)) return KD_ERR_NULL;
+        if (out_w_dtype != KD_BF16 && out_w_dtype != KD_F32) return KD_ERR_UNSUPPORTED;
+        if (!aligned(grad_loss, 4) || !aligned(grad_H, 16) || !aligned(grad_W, 16) || !aligned(out_H, 16) ||
+            !aligned(out_W, 16))
+            return KD_ERR_ALIGN;
+        const int es = prob->dtype == KD_BF16 ? 2 : 4;
+        const int64_t nH = prob->T * prob->d, nW = prob->V * prob->d;   // d % 8 == 0: whole groups of 8
+        // in place is allowed only for the same element type
+        if (grad_H && out_H != grad_H && overlaps(grad_H, (size_t)nH * es, out_H, (size_t)nH * es)) return KD_ERR_VALUE;
+        if (grad_W && (out_w_dtype == KD_BF16 || out_W != (const void*)grad_W) &&
+            overlaps(grad_W, (size_t)nW * 4, out_W, (size_t)nW * (out_w_dtype == KD_BF16 ? 2 : 4)))
+            return KD_ERR_VALUE;
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
         (void)hipGetLastError();
-        const int es = prob->dtype == KD_BF16 ? 2 : 4;
-        if (grad_H && prob->T > 0) {
-            const int64_t n16 = prob->T * prob->d * es / 16;   // d % 8 == 0: whole 16-byte chunks
-            const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n16, kThreads), 4096);
+        auto blocks = [](int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(n / 8, kThreads), 4096)); };
+        if (grad_H && nH > 0) {
             if (es == 2)
-                hipLaunchKernelGGL(scale_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, s,
-                                   reinterpret_cast<u32x4*>(grad_H), n16, grad_loss);
+                hipLaunchKernelGGL((scale_kernel<bf16_t, bf16_t>), dim3(blocks(nH)), dim3(kThreads), 0, s, grad_H, out_H, nH,
+                                   grad_loss);
             else
-                hipLaunchKernelGGL(scale_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
-                                   reinterpret_cast<u32x4*>(grad_H), n16, grad_loss);
+                hipLaunchKernelGGL((scale_kernel<float, float>), dim3(blocks(nH)), dim3(kThreads), 0, s, grad_H, out_H, nH,
+                                   grad_loss);
         }
-        if (grad_W) {
-            const int64_t n16 = prob->V * prob->d * 4 / 16;
-            const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n16, kThreads), 4096);
-            hipLaunchKernelGGL(scale_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
-                               reinterpret_cast<u32x4*>(grad_W), n16, grad_loss);
+        if (grad_W && nW > 0) {
+            if (out_w_dtype == KD_BF16)
+                hipLaunchKernelGGL((scale_kernel<float, bf16_t>), dim3(blocks(nW)), dim3(kThreads), 0, s, grad_W, out_W, nW,
+                                   grad_loss);
+            else
+                hipLaunchKernelGGL((scale_kernel<float, float>), dim3(blocks(nW)), dim3(kThreads), 0, s, grad_W, out_W, nW,
+                                   grad_loss);
         }
         return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
     } catch (...) {

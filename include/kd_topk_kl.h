@@ -115,8 +115,10 @@ typedef struct {
 /* Chunk size used when prob->chunk == 0 (depends on d, V and dtype only). */
 int64_t kd_topk_kl_default_chunk(const kd_problem* prob);
 
-/* Bytes of workspace `op` needs for `prob`; writes them to *bytes.  The value
- * depends on (C, V, K, d, dtype), not on T. */
+/* Bytes of workspace `op` needs for `prob`; writes them to *bytes and returns
+ * KD_OK, or returns the status that the entry itself would return for an
+ * invalid `prob` or `op` (*bytes is then untouched).  The value depends on
+ * (C, V, K, d, dtype), not on T. */
 kd_status kd_topk_kl_workspace_size(const kd_problem* prob, kd_op op, size_t* bytes);
 
 /* Forward ([TH] "Fused chunked KL": per chunk, project, take the
@@ -139,9 +141,16 @@ kd_status kd_topk_kl_backward(const kd_problem* prob, const void* H, const void*
                               void* grad_H, float* grad_W,
                               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Forward and backward in one pass over the chunks (each chunk's logits are
- * projected once and reused for the loss and the gradients).  Same outputs as
- * the two calls above; lse and row_loss may be NULL. */
+/* Forward and backward in one pass over the chunks ([TH] "Fused Chunked KL
+ * Loss", item "Fused chunked KL": the output projection is fused into the
+ * loss and the positions are handled slice by slice, so neither the T x V
+ * student logits nor a T x V gradient ever exists).  Here each chunk's logits
+ * are projected once and reused for the loss and both gradients, instead of
+ * being recomputed in a separate backward pass.  grad_loss[1] is the upstream
+ * gradient (device fp32; NULL means 1).  Writes loss[1], grad_H[T, d] and
+ * grad_W[V, d] (overwritten, or added to with KD_FLAG_ACCUMULATE_GRAD_W) and,
+ * if non-NULL, lse[T] and row_loss[T], with the same values as the forward
+ * entry.  Errors as for the other entries. */
 kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W,
                            const int32_t* topk_idx, const void* topk_logit,
                            const uint8_t* ignore, const float* grad_loss,
@@ -156,15 +165,25 @@ kd_status kd_topk_kl_validate(const kd_problem* prob, const int32_t* topk_idx,
                               const void* topk_logit, const uint8_t* ignore,
                               int64_t* bad_count, void* stream);
 
-/* Multiplies grad_H[T, d] (element type `dtype`, rounded to nearest even)
- * and grad_W[V, d] (fp32) in place by the device scalar grad_loss[0].  For
- * callers that run kd_topk_kl_fused with grad_loss = NULL (g = 1) before the
- * upstream gradient is known -- an autograd function whose forward already
- * produced the gradients -- and apply g afterwards: G above, and so both
- * gradients, are proportional to g.  Either pointer may be NULL to skip that
- * array; grad_W must not hold other accumulated gradients. */
-kd_status kd_topk_kl_scale_grads(const kd_problem* prob, const float* grad_loss, void* grad_H, float* grad_W,
-                                 void* stream);
+/* Writes out_H = g * grad_H and out_W = g * grad_W, g = grad_loss[0] (device
+ * fp32; NULL means 1).  For callers that run kd_topk_kl_fused with
+ * grad_loss = NULL (g = 1) before the upstream gradient is known -- an
+ * autograd function whose forward already produced the gradients -- and apply
+ * g afterwards: G, and so both gradients, are proportional to g.
+ *   grad_H, out_H  [T, d] element type `dtype` (rounded to nearest even);
+ *                  out_H may be grad_H itself (in place).
+ *   grad_W         [V, d] fp32, as the backward and fused entries leave it.
+ *   out_W          [V, d] fp32 (out_w_dtype = KD_F32; may be grad_W itself) or
+ *                  bf16 (out_w_dtype = KD_BF16, rounded to nearest even: the
+ *                  weight's own type for a bf16 model; must not overlap grad_W).
+ * Each input/output pair may be NULL (both) to skip it; out of place, the
+ * inputs are left untouched, so the kept gradients can be scaled again by
+ * another g.  Only prob->T, d, V, dtype are used (checked as elsewhere).
+ * Errors: KD_ERR_NULL (one of a pair missing), KD_ERR_ALIGN (16 bytes for the
+ * arrays, 4 for grad_loss), KD_ERR_UNSUPPORTED (out_w_dtype unknown),
+ * KD_ERR_VALUE (an output partly overlaps its input). */
+kd_status kd_topk_kl_scale_grads(const kd_problem* prob, const float* grad_loss, const void* grad_H,
+                                 const float* grad_W, void* out_H, void* out_W, int32_t out_w_dtype, void* stream);
 
 /* Kernel stages of every call, for timing. */
 typedef enum {

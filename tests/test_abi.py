@@ -205,13 +205,30 @@ def test_bf16_logit_alignment(lib):
 
 
 def test_scale_grads_argument_errors(lib):
-    p = prob()
-    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), None, P16, P16b, None) == B.KD_ERR_NULL
-    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), MIS, P16, P16b, None) == B.KD_ERR_ALIGN
-    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), P4, P4, P16b, None) == B.KD_ERR_ALIGN
-    assert lib.kd_topk_kl_scale_grads(ctypes.byref(p), P4, P16, P4, None) == B.KD_ERR_ALIGN
-    assert lib.kd_topk_kl_scale_grads(ctypes.byref(prob(tau=0.0)), P4, P16, P16b, None) == B.KD_ERR_VALUE
-    assert lib.kd_topk_kl_scale_grads(None, P4, P16, P16b, None) == B.KD_ERR_NULL
+    p = prob()          # grad_H 64 x 64 bf16 (8 KiB), grad_W 1000 x 64 fp32 (250 KiB)
+    F32, BF = B.KD_F32, B.KD_BF16
+    sg = lib.kd_topk_kl_scale_grads
+    P16c = ctypes.c_void_p(0x300000)
+    P16d = ctypes.c_void_p(0x400000)
+    # one of a pair missing
+    assert sg(ctypes.byref(p), P4, P16, P16b, None, P16d, F32, None) == B.KD_ERR_NULL
+    assert sg(ctypes.byref(p), P4, P16, P16b, P16c, None, F32, None) == B.KD_ERR_NULL
+    assert sg(ctypes.byref(p), None, None, P16b, None, None, F32, None) == B.KD_ERR_NULL
+    # alignment
+    assert sg(ctypes.byref(p), MIS, P16, P16b, P16c, P16d, F32, None) == B.KD_ERR_ALIGN
+    assert sg(ctypes.byref(p), P4, P4, P16b, P16c, P16d, F32, None) == B.KD_ERR_ALIGN
+    assert sg(ctypes.byref(p), P4, P16, P4, P16c, P16d, F32, None) == B.KD_ERR_ALIGN
+    assert sg(ctypes.byref(p), P4, P16, P16b, P4, P16d, F32, None) == B.KD_ERR_ALIGN
+    assert sg(ctypes.byref(p), P4, P16, P16b, P16c, P4, BF, None) == B.KD_ERR_ALIGN
+    # problem checks and the output type
+    assert sg(ctypes.byref(prob(tau=0.0)), P4, P16, P16b, P16c, P16d, F32, None) == B.KD_ERR_VALUE
+    assert sg(None, P4, P16, P16b, P16c, P16d, F32, None) == B.KD_ERR_NULL
+    assert sg(ctypes.byref(p), P4, P16, P16b, P16c, P16d, 7, None) == B.KD_ERR_UNSUPPORTED
+    # outputs that partly overlap their inputs (in place is the same pointer, same type)
+    assert sg(ctypes.byref(p), P4, P16, None, ctypes.c_void_p(0x100000 + 4096), None, F32, None) == B.KD_ERR_VALUE
+    assert sg(ctypes.byref(p), P4, None, P16b, None, P16b, BF, None) == B.KD_ERR_VALUE
+    assert sg(ctypes.byref(p), P4, None, P16b, None, ctypes.c_void_p(0x200000 + 65536), F32, None) == \
+        B.KD_ERR_VALUE
 
 
 def test_status_strings(lib):

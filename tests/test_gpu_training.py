@@ -1,6 +1,8 @@
 """GPU checks of the training-step integration: the autograd function (both
-modes), grad_W accumulation into a caller's buffer, a bf16 teacher-logit cache
-and in-place gradient scaling -- each against the fp64 oracle.
+modes, a retained graph differentiated twice, inputs that need no gradient),
+grad_W accumulation into a caller's buffer, a bf16 teacher-logit cache and
+gradient scaling in place and into fresh (bf16) outputs -- each against the
+fp64 oracle.
 """
 import numpy as np
 import pytest
@@ -139,7 +141,7 @@ def test_scale_grads_matches_upstream_gradient(problem):
     g = torch.tensor([2.5], device="cuda")
     _, gH1, gW1, _, _ = B.kd_topk_kl_fused(dev["H"], dev["W"], dev["topk_idx"], dev["topk_logit"], ign,
                                            temperature=1.5, chunk=CHUNK)
-    B.kd_topk_kl_scale_grads(g, gH1, gW1)
+    B.kd_topk_kl_scale_grads(g, gH1, gW1)           # in place
     loss, gH2, gW2, _, _ = B.kd_topk_kl_fused(dev["H"], dev["W"], dev["topk_idx"], dev["topk_logit"], ign,
                                               grad_loss=g, temperature=1.5, chunk=CHUNK)
     torch.cuda.synchronize()
@@ -149,3 +151,74 @@ def test_scale_grads_matches_upstream_gradient(problem):
     # of the largest element each)
     assert rel_maxabs(f64(gW1), f64(gW2)) <= 4e-3
     assert rel_maxabs(f64(gH1), f64(gH2)) <= 3 * 2.0 ** -8
+
+
+@pytest.mark.parametrize("mode", ["fused", "recompute"])
+def test_autograd_retained_graph_two_backwards(problem, mode):
+    """(a * loss).backward(retain_graph=True) then (b * loss).backward(): each
+    call's gradients are the oracle's times its own upstream gradient."""
+    x, ref = problem
+    dev = upload(x)
+    H = dev["H"].clone().requires_grad_(True)
+    W = dev["W"].clone().requires_grad_(True)
+    ign = torch.from_numpy(x.ignore).cuda()
+    loss = topk_kl_loss(H, W, dev["topk_idx"], dev["topk_logit"], ign, temperature=1.5, chunk=CHUNK, mode=mode)
+    (2.0 * loss).backward(retain_graph=True)
+    gH1, gW1 = H.grad.clone(), W.grad.clone()
+    H.grad, W.grad = None, None
+    (-0.5 * loss).backward()
+    torch.cuda.synchronize()
+    check(f"{mode}, first backward (g = 2)", float(loss.item()), f64(gH1), f64(gW1), ref, g=2.0)
+    check(f"{mode}, second backward (g = -0.5)", float(loss.item()), f64(H.grad), f64(W.grad), ref, g=-0.5)
+
+
+def test_autograd_without_gradients_runs_the_forward_only(problem):
+    """Neither input requires a gradient: the loss alone, no gradient buffers
+    (the peak allocation stays far below one grad_W)."""
+    x, ref = problem
+    dev = upload(x)
+    ign = torch.from_numpy(x.ignore).cuda()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    loss = topk_kl_loss(dev["H"], dev["W"], dev["topk_idx"], dev["topk_logit"], ign, temperature=1.5, chunk=CHUNK)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    grad_w_bytes = x.V * x.d * 4
+    say(f"  no-grad call: loss rel {loss_rel(float(loss.item()), ref['loss']):.2e}, "
+        f"peak above inputs {extra} B (one fp32 grad_W: {grad_w_bytes} B)")
+    assert not loss.requires_grad
+    assert loss_rel(float(loss.item()), ref["loss"]) <= BF16_TOL["loss"]
+    assert extra < grad_w_bytes // 4
+    # only H requires a gradient: W.grad stays None, H.grad is the oracle's
+    H = dev["H"].clone().requires_grad_(True)
+    loss = topk_kl_loss(H, dev["W"], dev["topk_idx"], dev["topk_logit"], ign, temperature=1.5, chunk=CHUNK)
+    loss.backward()
+    torch.cuda.synchronize()
+    assert rel_maxabs(f64(H.grad), ref["grad_H"]) <= BF16_TOL["grad"]
+
+
+def test_scale_grads_into_fresh_outputs(problem):
+    """Out of place: the kept fp32 gradients are untouched, out_H = g grad_H,
+    and a bf16 out_W is g grad_W rounded to nearest even."""
+    x, ref = problem
+    dev = upload(x)
+    ign = torch.from_numpy(x.ignore).cuda()
+    _, gH, gW, _, _ = B.kd_topk_kl_fused(dev["H"], dev["W"], dev["topk_idx"], dev["topk_logit"], ign,
+                                         temperature=1.5, chunk=CHUNK)
+    gH0, gW0 = gH.clone(), gW.clone()
+    g = torch.tensor([-1.75], device="cuda")
+    oH = torch.empty_like(gH)
+    oW = torch.empty(gW.shape, dtype=torch.bfloat16, device="cuda")
+    B.kd_topk_kl_scale_grads(g, gH, gW, out_H=oH, out_W=oW)
+    oW32 = torch.empty_like(gW)
+    B.kd_topk_kl_scale_grads(g, grad_W=gW, out_W=oW32)
+    torch.cuda.synchronize()
+    assert torch.equal(gH, gH0) and torch.equal(gW, gW0)
+    assert torch.equal(oW, (gW0 * -1.75).to(torch.bfloat16))     # fp32 product, then one rounding
+    assert torch.equal(oW32, gW0 * -1.75)
+    assert torch.equal(oH, (gH0.float() * -1.75).to(torch.bfloat16))
+    eH = rel_maxabs(f64(oH), -1.75 * ref["grad_H"])
+    eW = rel_maxabs(f64(oW), -1.75 * ref["grad_W"])
+    say(f"  scaled into fresh outputs, g = -1.75: grad_H {eH:.2e}  grad_W (bf16) {eW:.2e}")
+    assert eH <= BF16_TOL["grad"] and eW <= BF16_TOL["grad"]
