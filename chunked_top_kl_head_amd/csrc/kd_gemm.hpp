@@ -1,4 +1,5 @@
-// kd_gemm.hpp -- LDS-tiled MFMA GEMM engine for gfx950 (wave64, CDNA4).
+// kd_gemm.hpp -- shared GEMM definitions (operands, tile order) and the
+// register-staged MFMA engine for fp32 operands on gfx950 (wave64, CDNA4).
 //
 // Computes a BM x BN output tile  D[m, n] = sum_k A[m, k] B[k, n]  per
 // workgroup of 256 threads (2 x 2 waves, each owning a (BM/2) x (BN/2) block
@@ -11,18 +12,17 @@
 // M-indices of one N column: the stores of all three epilogues are then 8- or
 // 16-byte vectors along the contiguous dimension of the destination.
 //
-// bf16 uses v_mfma_f32_32x32x16_bf16 (the gfx950 shape that sustains the
-// dense bf16 rate); fp32 uses v_mfma_f32_32x32x2f32.
+// This engine serves fp32 operands only (v_mfma_f32_32x32x2f32); bf16
+// operands run on the direct-to-LDS engine of kd_gemm_dtl.hpp.
 //
 // Operands reach LDS through registers.  K-contiguous operands are copied as
 // 16-byte chunks; MN-contiguous operands are loaded as 16-byte vectors along
-// M, transposed in registers (8 x 8 for bf16, 4 x 4 for fp32) and stored as
-// K-contiguous chunks, so every MFMA fragment read is one ds_read_b128 per
-// lane.  Tiles are double buffered in LDS with one barrier per K step; the
-// per-thread offsets of all loads are loop invariant and the K position costs
-// one add per load.  Raw buffer loads return zero outside each operand's
-// extent, which handles the M/N tails; the K tail of the last step masks
-// offsets explicitly.
+// M, transposed in registers (4 x 4) and stored as K-contiguous chunks, so
+// every MFMA fragment read is one ds_read_b128 per lane.  Tiles are double
+// buffered in LDS with one barrier per K step; the per-thread offsets of all
+// loads are loop invariant and the K position costs one add per load.  Raw
+// buffer loads return zero outside each operand's extent, which handles the
+// M/N tails; the K tail of the last step masks offsets explicitly.
 #pragma once
 
 #include "kd_common.hpp"
@@ -159,28 +159,14 @@ template <typename E, int ROWS> struct TileLoader<E, ROWS, false> {
         }
     }
     __device__ __forceinline__ void store(lds_t* lds) const {
+        static_assert(EPC == 4, "fp32 operands: 4 x 4 blocks");
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            if constexpr (EPC == 8) {
-                // 8 x 8 transpose of 16-bit elements: out[mm] holds k = 0..7 of column mm.
+            // 4 x 4 transpose: out[mm] holds k = 0..3 of column mm
 #pragma unroll
-                for (int mm = 0; mm < 8; ++mm) {
-                    u32x4 o;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t lo = reg[i][2 * j][mm >> 1];
-                        const uint32_t hi = reg[i][2 * j + 1][mm >> 1];
-                        o[j] = (mm & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u))
-                                        : ((lo & 0xFFFFu) | (hi << 16));
-                    }
-                    lds_write16(lds, lds_off(mb[i] * 8 + mm, kc[i]), o);
-                }
-            } else {
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    u32x4 o = {reg[i][0][mm], reg[i][1][mm], reg[i][2][mm], reg[i][3][mm]};
-                    lds_write16(lds, lds_off(mb[i] * 4 + mm, kc[i]), o);
-                }
+            for (int mm = 0; mm < 4; ++mm) {
+                u32x4 o = {reg[i][0][mm], reg[i][1][mm], reg[i][2][mm], reg[i][3][mm]};
+                lds_write16(lds, lds_off(mb[i] * 4 + mm, kc[i]), o);
             }
         }
     }
@@ -230,18 +216,11 @@ template <typename E, int BM, int BN> struct WaveMma {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    if constexpr (Elem<E>::size == 2) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, a[cur][i]), __builtin_bit_cast(bf16x8, b[cur][j]),
-                            acc[i][j], 0, 0, 0);
-                    } else {
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                __uint_as_float(a[cur][i][e]), __uint_as_float(b[cur][j][e]), acc[i][j], 0, 0, 0);
-                    }
-                }
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            __uint_as_float(a[cur][i][e]), __uint_as_float(b[cur][j][e]), acc[i][j], 0, 0, 0);
         }
     }
 
@@ -263,6 +242,7 @@ constexpr int gemm_lds_bytes() { return 2 * (BM + BN) * 128; }
 template <typename E, int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, class Epi>
 __device__ __forceinline__ void gemm_body(const Operand& A, const Operand& B, const GemmGeom& g,
                                           const typename Epi::Params& ep, lds_t* smem) {
+    static_assert(Elem<E>::size == 4, "bf16 operands run on the direct-to-LDS engine");
     constexpr int ES = Elem<E>::size;
     constexpr int BK = 128 / ES;
     int tm, tn;
