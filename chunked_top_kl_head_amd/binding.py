@@ -29,6 +29,7 @@ EXPORTS = (
     "kd_topk_kl_forward",
     "kd_topk_kl_backward",
     "kd_topk_kl_fused",
+    "kd_topk_kl_fused_noalloc",
     "kd_topk_kl_validate",
     "kd_topk_kl_scale_grads",
     "kd_topk_kl_set_stage_events",
@@ -87,6 +88,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kd_topk_kl_backward.restype = ctypes.c_int
     lib.kd_topk_kl_fused.argtypes = [prob, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_topk_kl_fused.restype = ctypes.c_int
+    lib.kd_topk_kl_fused_noalloc.argtypes = [prob, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kd_topk_kl_fused_noalloc.restype = ctypes.c_int
     lib.kd_topk_kl_validate.argtypes = [prob, vp, vp, vp, vp, vp]
     lib.kd_topk_kl_validate.restype = ctypes.c_int
     lib.kd_topk_kl_scale_grads.argtypes = [prob, vp, vp, vp, vp, vp, ctypes.c_int32, vp]
@@ -226,6 +229,21 @@ def kd_topk_kl_fused(H, W, topk_idx, topk_logit, ignore=None, grad_loss=None, te
                                          _ptr(gW), _ptr(ws), ws.numel(), _stream(stream))
     _check("kd_topk_kl_fused", st)
     return loss, gH, gW, lse, rl
+
+
+def kd_topk_kl_fused_noalloc(H, W, topk_idx, topk_logit, ignore=None, *, loss, grad_H, grad_W, grad_loss=None,
+                             lse=None, row_loss=None, temperature=1.0, chunk=0, accumulate=False, stream=None):
+    """The fused entry on the library's static scratch: the caller passes every
+    output (loss[1], grad_H [T, d], grad_W [V, d] fp32, optional lse and
+    row_loss [T]); nothing is allocated here or in the library."""
+    T, d, V, K = _prep(H, W, topk_idx, topk_logit, ignore)
+    prob = problem(T, d, V, K, temperature, H.dtype, chunk, _flags(topk_logit, accumulate))
+    st = load_library().kd_topk_kl_fused_noalloc(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(topk_idx),
+                                                 _ptr(topk_logit), _ptr(ignore), _ptr(grad_loss), _ptr(loss),
+                                                 _ptr(lse), _ptr(row_loss), _ptr(grad_H), _ptr(grad_W),
+                                                 _stream(stream))
+    _check("kd_topk_kl_fused_noalloc", st)
+    return loss, grad_H, grad_W, lse, row_loss
 
 
 def kd_topk_kl_validate(topk_idx, topk_logit, V, ignore=None, stream=None) -> torch.Tensor:

@@ -28,6 +28,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "kd_kernels.hpp"
 #include "kd_topk_select.hpp"
@@ -442,6 +443,82 @@ static kd_status check_common(const kd_problem* p, kd_op op, const void* H, cons
     return KD_OK;
 }
 
+// Argument checks of the fused entry that do not involve its workspace.
+static kd_status fused_args(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
+                            const void* topk_logit, const float* grad_loss, const float* loss, const float* lse,
+                            const float* row_loss, const void* grad_H, const float* grad_W, Plan* pl) {
+    kd_status st = make_plan(prob, KD_OP_FUSED, pl);
+    if (st != KD_OK) return st;
+    if (!W) return KD_ERR_NULL;
+    if (prob->T > 0 && (!H || !topk_idx || !topk_logit)) return KD_ERR_NULL;
+    if (!loss || !grad_W || (prob->T > 0 && !grad_H)) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(topk_idx, 4) || !aligned(topk_logit, pl->logit_bf16 ? 2 : 4))
+        return KD_ERR_ALIGN;
+    if (!aligned(loss, 4) || !aligned(lse, 4) || !aligned(row_loss, 4) || !aligned(grad_loss, 4) ||
+        !aligned(grad_H, 16) || !aligned(grad_W, 16))
+        return KD_ERR_ALIGN;
+    return KD_OK;
+}
+
+// The fused entry's body, shared by the workspace and no-allocation entries.
+static kd_status fused_entry(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
+                             const void* topk_logit, const uint8_t* ignore, const float* grad_loss, float* loss,
+                             float* lse, float* row_loss, void* grad_H, float* grad_W, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    Plan pl;
+    kd_status st = fused_args(prob, H, W, topk_idx, topk_logit, grad_loss, loss, lse, row_loss, grad_H, grad_W, &pl);
+    if (st != KD_OK) return st;
+    if (pl.total > 0 && !workspace) return KD_ERR_NULL;
+    if (!aligned(workspace, 16)) return KD_ERR_ALIGN;
+    if (workspace_bytes < pl.total) return KD_ERR_WORKSPACE;
+    return dispatch(pl, prob->dtype, KD_OP_FUSED, H, W, topk_idx, topk_logit, ignore, grad_loss, loss, nullptr, lse,
+                    row_loss, grad_H, grad_W, workspace, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry: one static array per device, holding
+// the fused entry's workspace.  In host code `scratch` names a host-side
+// stand-in; its device address is looked up once per device (with that
+// device current) and only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static kd_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KD_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KD_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KD_OK;
+}
+
+// Largest chunk (at most the default chunk and the positions rounded up to
+// 64) whose fused workspace fits the scratch; 0 if none does.
+static int64_t scratch_chunk(const kd_problem& p) {
+    const int64_t top = std::min<int64_t>(default_chunk(p.d, p.V, p.dtype == KD_BF16 ? 2 : 4),
+                                          std::max<int64_t>(64, cdiv(p.T, 64) * 64));
+    kd_problem q = p;
+    auto fits = [&](int64_t C) {
+        q.chunk = C;
+        Plan pl;
+        return make_plan(&q, KD_OP_FUSED, &pl) == KD_OK && pl.total <= kScratchBytes;
+    };
+    for (int64_t C = top; C >= 64; C -= 64)
+        if (fits(C)) return C;
+    for (int64_t C = 63; C >= 1; --C)
+        if (fits(C)) return C;
+    return 0;
+}
+
 extern "C" {
 
 int64_t kd_topk_kl_default_chunk(const kd_problem* prob) {
@@ -501,15 +578,34 @@ kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W,
                            float* lse, float* row_loss, void* grad_H, float* grad_W, void* workspace,
                            size_t workspace_bytes, void* stream) {
     try {
+        return fused_entry(prob, H, W, topk_idx, topk_logit, ignore, grad_loss, loss, lse, row_loss, grad_H, grad_W,
+                           workspace, workspace_bytes, stream);
+    } catch (...) {
+        return KD_ERR_INTERNAL;
+    }
+}
+
+kd_status kd_topk_kl_fused_noalloc(const kd_problem* prob, const void* H, const void* W, const int32_t* topk_idx,
+                                   const void* topk_logit, const uint8_t* ignore, const float* grad_loss,
+                                   float* loss, float* lse, float* row_loss, void* grad_H, float* grad_W,
+                                   void* stream) {
+    try {
+        if (!prob) return KD_ERR_NULL;
+        kd_problem p = *prob;
         Plan pl;
-        kd_status st = check_common(prob, KD_OP_FUSED, H, W, topk_idx, topk_logit, workspace, workspace_bytes, &pl);
+        kd_status st = fused_args(&p, H, W, topk_idx, topk_logit, grad_loss, loss, lse, row_loss, grad_H, grad_W, &pl);
         if (st != KD_OK) return st;
-        if (!loss || !grad_W || (prob->T > 0 && !grad_H)) return KD_ERR_NULL;
-        if (!aligned(loss, 4) || !aligned(lse, 4) || !aligned(row_loss, 4) || !aligned(grad_loss, 4) ||
-            !aligned(grad_H, 16) || !aligned(grad_W, 16))
-            return KD_ERR_ALIGN;
-        return dispatch(pl, prob->dtype, KD_OP_FUSED, H, W, topk_idx, topk_logit, ignore, grad_loss, loss, nullptr,
-                        lse, row_loss, grad_H, grad_W, workspace, stream);
+        if (p.chunk == 0) {
+            p.chunk = scratch_chunk(p);
+            if (p.chunk == 0) return KD_ERR_WORKSPACE;   // not even one row fits
+        } else if (pl.total > kScratchBytes) {
+            return KD_ERR_WORKSPACE;
+        }
+        void* ws = nullptr;
+        st = scratch_of_current_device(&ws);
+        if (st != KD_OK) return st;
+        return fused_entry(&p, H, W, topk_idx, topk_logit, ignore, grad_loss, loss, lse, row_loss, grad_H, grad_W,
+                           ws, kScratchBytes, stream);
     } catch (...) {
         return KD_ERR_INTERNAL;
     }
@@ -669,7 +765,9 @@ const char* kd_status_string(kd_status status) {
         case KD_ERR_SHAPE: return "invalid shape (T, d, V, K or chunk)";
         case KD_ERR_VALUE: return "invalid value (temperature must be finite and > 0; flags known; reserved 0)";
         case KD_ERR_ALIGN: return "misaligned pointer";
-        case KD_ERR_WORKSPACE: return "workspace smaller than kd_topk_kl_workspace_size";
+        case KD_ERR_WORKSPACE:
+            return "workspace too small (below kd_topk_kl_workspace_size, or beyond the 256 MiB static scratch "
+                   "of kd_topk_kl_fused_noalloc)";
         case KD_ERR_UNSUPPORTED: return "unsupported problem (dtype, d % 8, K > 1024 or size limits)";
         case KD_ERR_HIP: return "HIP launch failure";
         case KD_ERR_INTERNAL: return "internal error";

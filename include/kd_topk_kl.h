@@ -158,6 +158,30 @@ kd_status kd_topk_kl_fused(const kd_problem* prob, const void* H, const void* W,
                            void* grad_H, float* grad_W,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* The fused entry without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and errors as
+ * kd_topk_kl_fused otherwise.  Its workspace is a static 256 MiB device
+ * array of the library, one per GPU, held from the library's first use on
+ * that GPU until the process ends; the call uses the array of the current
+ * device (`stream` must belong to it) and allocates nothing.
+ *   - prob->chunk == 0: the largest chunk (at most the default chunk and the
+ *     positions rounded up to 64) whose fused workspace fits 256 MiB, e.g.
+ *     about 600 rows at a 201,088-token vocabulary.  A problem whose workspace
+ *     exceeds 256 MiB even for one row, or an explicit chunk whose workspace
+ *     exceeds it (kd_topk_kl_workspace_size(prob, KD_OP_FUSED) > 256 MiB),
+ *     returns KD_ERR_WORKSPACE with nothing enqueued.
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     behind; each call rewrites whatever it reads there first, so nothing
+ *     needs clearing between calls.  Calls that overlap in time on one GPU
+ *     (different streams or threads) race on the array and must be ordered
+ *     by the caller. */
+kd_status kd_topk_kl_fused_noalloc(const kd_problem* prob, const void* H, const void* W,
+                                   const int32_t* topk_idx, const void* topk_logit,
+                                   const uint8_t* ignore, const float* grad_loss,
+                                   float* loss, float* lse, float* row_loss,
+                                   void* grad_H, float* grad_W, void* stream);
+
 /* Debug check of the cache preconditions: writes to bad_count[0] (device
  * int64) the number of ids outside [0, V) plus the number of kept positions
  * whose teacher logits are all -inf or contain NaN. */

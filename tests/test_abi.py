@@ -126,6 +126,27 @@ def call_fused(lib, p, H=P16, W=P16b, idx=P4, lg=P4, ig=None, g=None, loss=P4, l
     return lib.kd_topk_kl_fused(ctypes.byref(p), H, W, idx, lg, ig, g, loss, lse, rl, gH, gW, ws, wsb, None)
 
 
+def call_noalloc(lib, p, H=P16, W=P16b, idx=P4, lg=P4, ig=None, g=None, loss=P4, lse=None, rl=None, gH=P16,
+                 gW=P16b):
+    return lib.kd_topk_kl_fused_noalloc(ctypes.byref(p), H, W, idx, lg, ig, g, loss, lse, rl, gH, gW, None)
+
+
+def test_noalloc_argument_errors(lib):
+    """Checked before the scratch is looked up, so no GPU is needed."""
+    big = prob(T=20000, d=2880, V=201088, K=100, chunk=8192)     # 3.3 GB of workspace at this chunk
+    assert call_noalloc(lib, big) == B.KD_ERR_WORKSPACE
+    assert lib.kd_topk_kl_fused_noalloc(None, P16, P16b, P4, P4, None, None, P4, None, None, P16, P16b,
+                                        None) == B.KD_ERR_NULL
+    assert call_noalloc(lib, prob(K=0)) == B.KD_ERR_SHAPE
+    assert call_noalloc(lib, prob(tau=0.0)) == B.KD_ERR_VALUE
+    assert call_noalloc(lib, prob(), H=None) == B.KD_ERR_NULL
+    assert call_noalloc(lib, prob(), loss=None) == B.KD_ERR_NULL
+    assert call_noalloc(lib, prob(), gW=None) == B.KD_ERR_NULL
+    assert call_noalloc(lib, prob(), H=P4) == B.KD_ERR_ALIGN
+    assert call_noalloc(lib, prob(), gH=P4) == B.KD_ERR_ALIGN
+    assert call_noalloc(lib, prob(), lse=MIS) == B.KD_ERR_ALIGN
+
+
 def test_forward_argument_errors(lib):
     p = prob()
     assert call_fwd(lib, p, H=None) == B.KD_ERR_NULL

@@ -130,3 +130,15 @@ def test_m0_check_catches_a_foreign_use():
     assert len(check_m0_discipline(late)[0]) == 2
     other = {"k": ["s_mov_b32 m0, s4", "s_nop 0", "buffer_load_dwordx4 v1, s[0:3], 0 offen lds", "s_mov_b32 s5, m0"]}
     assert len(check_m0_discipline(other)[0]) == 1
+
+
+def test_library_sources_allocate_nothing():
+    """The library takes every buffer from its caller (or its static scratch):
+    no device or host allocation call appears in its sources."""
+    csrc = os.path.join(ROOT, "chunked_top_kl_head_amd", "csrc")
+    pat = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipExtMalloc\w*|hipMallocAsync|malloc|calloc|"
+                     r"new\s+\w+\s*\[)\s*\(?")
+    for f in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, f)).read()
+        code = re.sub(r"//[^\n]*", "", text)
+        assert not pat.search(code), (f, pat.search(code).group(0))
