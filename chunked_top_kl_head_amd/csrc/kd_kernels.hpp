@@ -14,6 +14,7 @@
 #pragma once
 
 #include "kd_gemm_dtl.hpp"
+#include "kd_topk_select.hpp"
 
 namespace kd {
 
@@ -251,7 +252,13 @@ struct RawLogitsParams {
     float* out;
     int64_t ld;
     int V, rows;
+    uint32_t* bmax;   // optional (bf16 engine) [rows][nblk]: a record never below the largest select order key
+                      // of each 128-id block (0 for blocks beyond V)
+    int nblk;
 };
+
+// True when the wave half wm of the 256-id tile at m0 holds no id below V.
+__device__ __forceinline__ bool v0_all_padding(int m0, int wm, int V) { return m0 + 128 * wm >= V; }
 
 template <typename E, int BM, int BN> struct RawLogitsEpi {
     using Params = RawLogitsParams;
@@ -261,6 +268,39 @@ template <typename E, int BM, int BN> struct RawLogitsEpi {
     static __device__ __forceinline__ void apply(Mma& mma, int m0, int n0, int, int wm, int wn, int lane, int tid,
                                                  lds_t* smem, const Params& p) {
         constexpr int FM = Mma::FM, FN = Mma::FN;
+        static_assert(BM == 2 * kSelBlock, "one 128-id block per wave half of the tile");
+        if (kStaged && p.bmax) {
+            // this wave's 128 ids of each of its chunk rows: the select order
+            // key of their largest value (a float max; a zero is recorded as
+            // +0 and a block of NaNs as the lowest key, so the record is never
+            // below the block's largest key; ids at or beyond V are left out)
+            const int blk = (m0 / BM) * 2 + wm;
+            const bool tail = m0 + BM > p.V;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                float mv = -INFINITY;
+                if (!tail) {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) mv = fmaxf(mv, mma.acc[i][j][e]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int v0 = m0 + Mma::row(wm, i, q, lane);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (v0 + r < p.V) mv = fmaxf(mv, mma.acc[i][j][4 * q + r]);
+                        }
+                }
+                mv = halves_max(mv);
+                const uint32_t key = mv == 0.f ? sel_key(0u) : sel_key(__float_as_uint(mv));
+                const int t = n0 + Mma::col(wn, j, lane);
+                if (lane < 32 && t < p.rows) p.bmax[(int64_t)t * p.nblk + blk] = (v0_all_padding(m0, wm, p.V) ? 0u : key);
+            }
+        }
         if constexpr (kStaged) {
             // Two passes over halves of 128 vocabulary ids (held by the waves
             // with wm = half): the half tile goes to LDS as [t][128] fp32

@@ -381,7 +381,9 @@ static kd_status dispatch(const Plan& pl, int dtype, kd_op op, const void* H, co
 struct TeacherPlan {
     int64_t T, d, V, K, C, V_pad, ld;
     int es;
-    size_t total;
+    int64_t nblk;        // 128-id blocks per row (V_pad / 128)
+    bool blocks;         // select through the blocks' records (bf16 operands, nblk <= kSelMaxBlocks)
+    size_t off_bmax, total;
 };
 
 static kd_status teacher_plan(const kd_teacher_problem* p, TeacherPlan* out) {
@@ -400,7 +402,10 @@ static kd_status teacher_plan(const kd_teacher_problem* p, TeacherPlan* out) {
     q.ld = cdiv(q.V, 4) * 4;
     if (q.es == 4 && ((q.V_pad + BM) * q.d * q.es >= kOperandLimit || (q.C + BN) * q.d * q.es >= kOperandLimit))
         return KD_ERR_UNSUPPORTED;
-    q.total = align256((size_t)(q.C * q.ld) * sizeof(float));
+    q.nblk = q.V_pad / kSelBlock;
+    q.blocks = q.es == 2 && q.nblk <= kSelMaxBlocks;
+    q.off_bmax = align256((size_t)(q.C * q.ld) * sizeof(float));
+    q.total = q.off_bmax + (q.blocks ? align256((size_t)(q.C * q.nblk) * sizeof(uint32_t)) : 0);
     *out = q;
     return KD_OK;
 }
@@ -409,6 +414,7 @@ template <typename E>
 static kd_status run_teacher(const TeacherPlan& pl, const void* H, const void* W, int32_t* idx, float* val, void* ws,
                              hipStream_t stream) {
     float* z = static_cast<float*>(ws);
+    uint32_t* bmax = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.off_bmax);
     const int bk = 128 / pl.es;
     for (int64_t t0 = 0; t0 < pl.T; t0 += pl.C) {
         const int64_t rc = pl.T - t0 < pl.C ? pl.T - t0 : pl.C;
@@ -417,9 +423,14 @@ static kd_status run_teacher(const TeacherPlan& pl, const void* H, const void* W
         const GemmGeom g = geom(pl.V_pad, rc, pl.d, 1, bk);
         RawLogitsParams rp{};
         rp.out = z; rp.ld = pl.ld; rp.V = (int)pl.V; rp.rows = (int)rc;
+        rp.bmax = pl.blocks ? bmax : nullptr; rp.nblk = (int)pl.nblk;
         launch_gemm<E, true, true, false, RawLogitsEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, rp);
-        hipLaunchKernelGGL(topk_select_kernel<float>, dim3((unsigned)rc), dim3(kSelThreads), 0, stream, z, pl.ld,
-                           (int)pl.V, (int)pl.K, idx + t0 * pl.K, val + t0 * pl.K);
+        if (pl.blocks)
+            hipLaunchKernelGGL(topk_select_blocks_kernel, dim3((unsigned)rc), dim3(kSelThreads), 0, stream, z, pl.ld,
+                               (int)pl.V, (int)pl.K, bmax, (int)pl.nblk, idx + t0 * pl.K, val + t0 * pl.K);
+        else
+            hipLaunchKernelGGL(topk_select_kernel<float>, dim3((unsigned)rc), dim3(kSelThreads), 0, stream, z, pl.ld,
+                               (int)pl.V, (int)pl.K, idx + t0 * pl.K, val + t0 * pl.K);
     }
     return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
 }

@@ -172,6 +172,92 @@ __device__ __forceinline__ uint64_t sel_full(uint32_t key, int id) {
     return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)id);
 }
 
+// Steps 3'-4, shared by both select kernels: with n candidates collected (all
+// keys >= some bound, capped at kSelCap), an exact radix select over the full
+// row when n is outside [K, kSelCap], then the bitonic sort and the output.
+template <typename E>
+__device__ __forceinline__ void sel_finish(const char* row, int V, int K, int64_t t, int tid, uint32_t n, uint64_t* cand,
+                           uint32_t* hist, uint32_t* part, uint32_t* count, int32_t* out_idx, float* out_val) {
+    auto collect = [&](uint64_t L) {
+        auto take = [&](uint32_t key, int id) {
+            const uint64_t k = sel_full(key, id);
+            if (k >= L) {
+                const uint32_t pos = atomicAdd(count, 1u);
+                if (pos < (uint32_t)kSelCap) cand[pos] = k;
+            }
+        };
+        if (L >> 63) sel_for_row_filtered<E>(row, V, tid, SelFilter<E>::threshold((uint32_t)(L >> 32)), take);
+        else         sel_for_row<E>(row, V, tid, take);
+        __syncthreads();
+    };
+    if (n < (uint32_t)K || n > (uint32_t)kSelCap) {
+        // exact: radix select over the 64-bit keys of the full row
+        uint64_t P = 0;
+        uint32_t above = 0;
+        int nb = 0;
+        __syncthreads();
+        while (true) {
+            for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0u;
+            __syncthreads();
+            const int sh = 56 - nb;
+            sel_for_row<E>(row, V, tid, [&](uint32_t key, int id) {
+                const uint64_t k = sel_full(key, id);
+                if (nb == 0 || (k >> (64 - nb)) == P) atomicAdd(&hist[(k >> sh) & 0xFFu], 1u);
+            });
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t acc = above;
+                int v = 0;
+                for (int d = 255; d >= 0; --d) {
+                    if (acc + hist[d] >= (uint32_t)K) { v = d; break; }
+                    acc += hist[d];
+                }
+                part[0] = (uint32_t)v;
+                part[1] = acc;
+                part[2] = acc + hist[v];
+            }
+            __syncthreads();
+            const uint32_t v = part[0];
+            above = part[1];
+            const uint32_t cnt = part[2];
+            P = (P << 8) | v;
+            nb += 8;
+            __syncthreads();
+            if (cnt <= (uint32_t)kSelCap || nb == 64) break;
+        }
+        if (tid == 0) *count = 0u;
+        __syncthreads();
+        collect(nb == 64 ? P : (P << (64 - nb)));
+        n = *count;
+    }
+
+    // bitonic sort of the candidates, descending (padding keys 0 sort last)
+    int n2 = 1;
+    while (n2 < (int)n) n2 <<= 1;
+    for (int i = (int)n + tid; i < n2; i += kSelThreads) cand[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < n2 / 2; i += kSelThreads) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a = cand[lo], b = cand[hi];
+                if ((a < b) == desc) {
+                    cand[lo] = b;
+                    cand[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int k = tid; k < K; k += kSelThreads) {
+        const uint64_t c = cand[k];
+        out_idx[t * K + k] = (int32_t)(~(uint32_t)c);
+        out_val[t * K + k] = sel_value((uint32_t)(c >> 32));
+    }
+}
+
 template <typename E>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const void* logits, int64_t ld, int V, int K,
                                                                   int32_t* out_idx, float* out_val) {
@@ -249,7 +335,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const void* lo
     }
 
     // 2. collect every key >= bound
-    auto collect = [&](uint64_t L) {
+    {
+        const uint64_t L = bound;
         auto take = [&](uint32_t key, int id) {
             const uint64_t k = sel_full(key, id);
             if (k >= L) {
@@ -260,75 +347,131 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const void* lo
         if (L >> 63) sel_for_row_filtered<E>(row, V, tid, SelFilter<E>::threshold((uint32_t)(L >> 32)), take);
         else         sel_for_row<E>(row, V, tid, take);
         __syncthreads();
-    };
-    collect(bound);
-    uint32_t n = count;
-    if (n < (uint32_t)K || n > (uint32_t)kSelCap) {
-        // 3'. exact: radix select over the 64-bit keys of the full row
-        uint64_t P = 0;
-        uint32_t above = 0;
-        int nb = 0;
-        __syncthreads();
-        while (true) {
-            for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0u;
-            __syncthreads();
-            const int sh = 56 - nb;
-            sel_for_row<E>(row, V, tid, [&](uint32_t key, int id) {
-                const uint64_t k = sel_full(key, id);
-                if (nb == 0 || (k >> (64 - nb)) == P) atomicAdd(&hist[(k >> sh) & 0xFFu], 1u);
-            });
-            __syncthreads();
-            if (tid == 0) {
-                uint32_t acc = above;
-                int v = 0;
-                for (int d = 255; d >= 0; --d) {
-                    if (acc + hist[d] >= (uint32_t)K) { v = d; break; }
-                    acc += hist[d];
-                }
-                part[0] = (uint32_t)v;
-                part[1] = acc;
-                part[2] = acc + hist[v];
-            }
-            __syncthreads();
-            const uint32_t v = part[0];
-            above = part[1];
-            const uint32_t cnt = part[2];
-            P = (P << 8) | v;
-            nb += 8;
-            __syncthreads();
-            if (cnt <= (uint32_t)kSelCap || nb == 64) break;
-        }
-        if (tid == 0) count = 0u;
-        __syncthreads();
-        collect(nb == 64 ? P : (P << (64 - nb)));
-        n = count;
     }
+    // 3, 4
+    sel_finish<E>(row, V, K, t, tid, count, cand, hist, part, &count, out_idx, out_val);
+}
 
-    // 4. bitonic sort of the candidates, descending (padding keys 0 sort last)
-    int n2 = 1;
-    while (n2 < (int)n) n2 <<= 1;
-    for (int i = (int)n + tid; i < n2; i += kSelThreads) cand[i] = 0ull;
+// ---------------------------------------------------------------------------
+// Select over fp32 rows that come with a record of every block of kSelBlock
+// consecutive values: bmax[t][b] is never below the largest order key of the
+// block (written by the producing logits contraction; blocks beyond V hold 0).
+// Bound: the lowest key of the 12-bit key bin in which the records, counted
+// from the top, reach K.  Every element with a key >= that bound sits in a
+// block whose record is >= it, so only those blocks are read (for a row of
+// Gaussian-like logits a few hundred of ceil(V / 128)), and every key >= the
+// bound in them is collected.  When each such record is exactly its block's
+// largest key (the usual case) there are at least K such keys; otherwise, or
+// when ties push the count beyond the buffer, the shared finish runs the exact
+// full-row select.  Requires nblk <= kSelMaxBlocks.
+// ---------------------------------------------------------------------------
+constexpr int kSelBlock = 128;
+constexpr int kSelMaxBlocks = 2048;
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_blocks_kernel(const float* logits, int64_t ld, int V,
+                                                                         int K, const uint32_t* bmax, int nblk,
+                                                                         int32_t* out_idx, float* out_val) {
+    __shared__ uint64_t cand[kSelCap];
+    static_assert(kSelBins * 4 <= kSelCap * 8, "histogram fits the candidate buffer");
+    __shared__ uint32_t bk[kSelMaxBlocks];     // block records
+    __shared__ uint32_t part[kSelThreads];
+    __shared__ uint32_t count, bin;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(cand);
+    const int t = (int)blockIdx.x;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const float* row = logits + (int64_t)t * ld;
+
+    // 1. the records and their 12-bit histogram
+    for (int b = tid; b < kSelBins; b += kSelThreads) hist[b] = 0u;
     __syncthreads();
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < n2 / 2; i += kSelThreads) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint64_t a = cand[lo], b = cand[hi];
-                if ((a < b) == desc) {
-                    cand[lo] = b;
-                    cand[hi] = a;
+    for (int b = tid; b < nblk; b += kSelThreads) {
+        const uint32_t k = bmax[(int64_t)t * nblk + b];
+        bk[b] = k;
+        atomicAdd(&hist[k >> 20], 1u);
+    }
+    __syncthreads();
+    // 2. the highest bin whose suffix count reaches K
+    {
+        constexpr int PER = kSelBins / kSelThreads;   // 16 bins per thread, thread 255 the highest
+        uint32_t local = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) local += hist[tid * PER + i];
+        part[tid] = local;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t acc = 0;
+            int bb = 0;
+            bool found = false;
+            for (int w = kSelThreads - 1; w >= 0 && !found; --w) {
+                if (acc + part[w] >= (uint32_t)K) {
+                    for (int i = PER - 1; i >= 0; --i) {
+                        acc += hist[w * PER + i];
+                        if (acc >= (uint32_t)K) { bb = w * PER + i; found = true; break; }
+                    }
+                } else {
+                    acc += part[w];
                 }
             }
-            __syncthreads();
+            bin = (uint32_t)bb;
+            count = 0u;
         }
+        __syncthreads();
     }
-    for (int k = tid; k < K; k += kSelThreads) {
-        const uint64_t c = cand[k];
-        out_idx[(int64_t)t * K + k] = (int32_t)(~(uint32_t)c);
-        out_val[(int64_t)t * K + k] = sel_value((uint32_t)(c >> 32));
+    const uint32_t B = bin << 20;
+    // 3. the blocks whose record is >= B, listed in bk (each thread first takes
+    // its own records into registers, so the list can overwrite them)
+    constexpr int RPT = kSelMaxBlocks / kSelThreads;
+    uint32_t rec[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int b = tid + i * kSelThreads;
+        rec[i] = b < nblk ? bk[b] : 0u;
     }
+    if (tid == 0) part[0] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int b = tid + i * kSelThreads;
+        if (b < nblk && rec[i] >= B) bk[atomicAdd(&part[0], 1u)] = (uint32_t)b;
+    }
+    __syncthreads();
+    const int nq = (int)part[0];
+    // every key >= B of the listed blocks: one half-wave per block, 16 bytes a
+    // lane, four blocks in flight
+    const uint64_t L = (uint64_t)B << 32;
+    const int hw = 2 * wave + (lane >> 5), hl = lane & 31;
+    constexpr int NHW = 2 * (kSelThreads / 64);
+    constexpr int U = 4;
+    for (int q0 = hw; q0 < nq; q0 += NHW * U) {
+        u32x4 v[U];
+        int id0[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * NHW;
+            id0[u] = q < nq ? (int)bk[q] * kSelBlock + 4 * hl : V;
+            if (id0[u] + 3 < V) {
+                v[u] = *reinterpret_cast<const u32x4*>(row + id0[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[u][e] = id0[u] + e < V ? __float_as_uint(row[id0[u] + e]) : 0x7FC00000u;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint64_t k = sel_full(sel_key(v[u][e]), id0[u] + e);
+                if (id0[u] + e < V && k >= L) {
+                    const uint32_t pos = atomicAdd(&count, 1u);
+                    if (pos < (uint32_t)kSelCap) cand[pos] = k;
+                }
+            }
+    }
+    __syncthreads();
+    // 4. sort, or the exact full-row select
+    sel_finish<float>(reinterpret_cast<const char*>(row), V, K, t, tid, count, cand, hist, part, &count, out_idx,
+                      out_val);
 }
 
 }  // namespace kd

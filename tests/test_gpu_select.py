@@ -122,10 +122,16 @@ def check_teacher(H64, W64, idx, val, K):
         assert np.isin(must, ids).all()
 
 
+# bf16 operands go through the select that reads only the 128-id blocks whose
+# record reaches the bound (with K above the number of blocks, or too many
+# candidates, it takes every block and may finish with the exact full-row
+# select); fp32 operands through the full-row select.
 @pytest.mark.parametrize("dtype,T,d,V,K,chunk", [
     ("bf16", 300, 256, 5000, 20, 128),     # three chunks, the last ragged; vocabulary tail in the last tile
-    ("bf16", 70, 136, 3001, 100, 0),       # V not a multiple of 4 (padded rows of the chunk buffer)
+    ("bf16", 200, 136, 20000, 100, 64),    # K close to the number of blocks (157)
+    ("bf16", 70, 136, 3001, 100, 0),       # V not a multiple of 4 (padded rows of the chunk buffer); K > blocks
     ("bf16", 33, 64, 37, 37, 16),          # K = V
+    ("f32", 130, 64, 3000, 10, 64),
     ("f32", 100, 64, 1000, 10, 64),
 ])
 def test_teacher_topk(dtype, T, d, V, K, chunk):
@@ -161,3 +167,33 @@ def test_teacher_topk_full_size():
     r = torch.from_numpy(rows).cuda()
     check_teacher(x.H[rows].astype(np.float64), x.W.astype(np.float64), idx[r].cpu().numpy(), val[r].cpu().numpy(), K)
     say(f"  {rows.size} sampled rows valid; all {x.T} rows ordered")
+
+
+def test_teacher_topk_heavy_ties():
+    """Every vocabulary row is one of three rows, so each position's logits take
+    three values, each on a third of the ids: every 128-id block reaches the
+    K-th largest block maximum and the candidates (3,000 equal logits) overflow
+    the buffer, which sends the rows to the exact full-row select.  The answer
+    is unique: the K smallest ids of the class with the largest logit."""
+    T, d, V, K = 40, 64, 9000, 50
+    rng = np.random.default_rng(11)
+    base = (rng.standard_normal((3, d)) * 0.05).astype(np.float32)
+    Hf = rng.standard_normal((T, d)).astype(np.float32)
+    Wf = base[np.arange(V) % 3]
+    from chunked_top_kl_head_amd import synth
+    H = torch.from_numpy(synth.f32_to_bf16_bits(Hf).view(np.int16).reshape(T, d)).cuda().view(torch.bfloat16)
+    W = torch.from_numpy(synth.f32_to_bf16_bits(Wf).view(np.int16).reshape(V, d)).cuda().view(torch.bfloat16)
+    idx, val = B.kd_teacher_topk(H, W, K, chunk=16)
+    torch.cuda.synchronize()
+    H64 = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(Hf)).reshape(T, d).astype(np.float64)
+    b64 = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(base)).reshape(3, d).astype(np.float64)
+    z = H64 @ b64.T                                   # [T, 3]
+    srt = np.sort(z, axis=1)
+    clear = (srt[:, 2] - srt[:, 1]) > 1e-3 * np.abs(srt[:, 2]).max()
+    idx_h, val_h = idx.cpu().numpy(), val.cpu().numpy()
+    for t in np.nonzero(clear)[0]:
+        c = int(np.argmax(z[t]))
+        expect = np.arange(c, V, 3)[:K]
+        assert np.array_equal(idx_h[t], expect), t
+        assert np.all(val_h[t] == val_h[t, 0])
+    say(f"  heavy ties: {int(clear.sum())} of {T} rows checked exactly")
