@@ -358,7 +358,9 @@ def main() -> int:
         with open(tfile) as fh:
             tr = json.load(fh)
         ent = tr.get(args.workload, {}).get(dom)
-        if ent and ent.get("source_sha") == kernel_source_hash() and ent.get("chunk") == chunk:
+        # the figures are per launch of the fused entry's kernels at one chunk size
+        if (ent and ent.get("source_sha") == kernel_source_hash() and ent.get("chunk") == chunk
+                and ent.get("mode", "fused") == args.mode):
             roof["traffic"] = ent["bytes_per_launch"]
 
     out = {
