@@ -252,6 +252,31 @@ def test_scale_grads_argument_errors(lib):
         B.KD_ERR_VALUE
 
 
+@pytest.mark.parametrize("name,splits", [("gptoss20b", 2), ("llama3b", 5)])
+def test_fused_workspace_layout(lib, name, splits):
+    """The fused workspace of a standard workload is the sum of the regions the
+    layout documents, with the grad_H contraction split over the vocabulary
+    `splits` ways (fewer than 512 output tiles: 12 x 32 = 384 at the
+    GPT-OSS-like shape, 12 x 4 = 48 at the Llama-like one) -- pinned so that
+    the documented layout and the code cannot drift apart."""
+    from chunked_top_kl_head_amd import synth
+    w = synth.WORKLOADS[name]
+    C, d, V, K = w.chunk, w.d, w.V, w.K
+    V_pad = (V + 255) // 256 * 256
+    a = lambda x: (x + 255) // 256 * 256
+    regions = [256,                                   # header (loss accumulator, N, s)
+               a(4 * C),                              # chunk row losses
+               a(8 * C * (V_pad // 128)),             # (reference, sum) per 128-id block
+               a(2 * C * V_pad),                      # G, bf16, blocked
+               a(4 * splits * C * d),                 # grad_H partials
+               a(8 * C * K),                          # cached-entry list
+               a(4 * C * K),                          # cached-id logits
+               a(4 * C), a(4 * C), a(C),              # references, row factors, dirty flags
+               a(2 * C * d)]                          # row-scaled H_c
+    st, n = ws_size(lib, prob(T=w.T, d=d, V=V, K=K, chunk=C), B.KD_OP_FUSED)
+    assert st == B.KD_OK and n == sum(regions)
+
+
 def test_status_strings(lib):
     for s in range(9):
         msg = lib.kd_status_string(s).decode()
