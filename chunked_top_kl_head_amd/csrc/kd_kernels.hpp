@@ -449,13 +449,25 @@ template <typename E, int BM, int BN> struct GradWEpi {
             constexpr int NK = RW / 2;            // 16-byte pieces per thread and half
             // this thread's pieces of grad_W: the first half's are read before
             // anything is staged, the second half's as the first half's stores
-            // free their registers, so the latency overlaps staging and barriers
-            auto load_old = [&](int half, int k) {
-                const int v = n0 + wave * RW + 2 * k + (lane >> 5);
+            // free their registers, so the latency overlaps staging and barriers.
+            // The tile's rows n0.. go through one buffer resource (at most
+            // 256 · 2^20 · 4 bytes, below kOOB): a piece past the hidden size
+            // gets the out-of-range offset and a row past V lies beyond
+            // num_records, so the hardware drops those stores and reads zeros
+            // (also everywhere when not accumulating).  Without branches the
+            // compiler counts the loads in flight exactly instead of waiting
+            // for every earlier store before each one (vmcnt(0)).
+            const int rows = min(256, p.V - n0);
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.gw + (int64_t)n0 * p.d, (uint32_t)rows * (uint32_t)p.d * 4u);
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.gw + (int64_t)n0 * p.d,
+                                                        p.accumulate ? (uint32_t)rows * (uint32_t)p.d * 4u : 0u);
+            auto off_of = [&](int half, int k) -> uint32_t {
+                const int vl = wave * RW + 2 * k + (lane >> 5);
                 const int h = m0 + 128 * half + 4 * c;
-                return (p.accumulate && v < p.V && h < p.d)
-                           ? *reinterpret_cast<const f32x4*>(p.gw + (int64_t)v * p.d + h)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+                return h < p.d ? ((uint32_t)vl * (uint32_t)p.d + (uint32_t)h) * 4u : kOOB;
+            };
+            auto load_old = [&](int half, int k) {
+                return __builtin_bit_cast(f32x4, buf_load16(rr, off_of(half, k)));
             };
             f32x4 old[NK];
 #pragma unroll
@@ -463,7 +475,6 @@ template <typename E, int BM, int BN> struct GradWEpi {
             __syncthreads();   // every wave is past its main loop: the stage LDS is free
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int h = m0 + 128 * half + 4 * c;
                 if (wm == half) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
@@ -486,9 +497,8 @@ template <typename E, int BM, int BN> struct GradWEpi {
                     const int vl = wave * RW + 2 * k + (lane >> 5);
                     const f32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
                         smem + vl * 512 + ((c ^ (vl & 31)) << 4));
-                    const int v = n0 + vl;
-                    if (v < p.V && h < p.d)
-                        *reinterpret_cast<f32x4*>(p.gw + (int64_t)v * p.d + h) = val + old[k];
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val + old[k]), rw,
+                                                           off_of(half, k), 0, 0);
                     if (half == 0) old[k] = load_old(1, k);
                 }
                 if (half == 0) __syncthreads();
