@@ -145,6 +145,68 @@ def bench_select(args) -> int:
     return 0
 
 
+def bench_mfma_ceiling(args) -> int:
+    """The part's sustained bf16 MFMA rate with no global memory traffic
+    (libkdprobe.so): 256 workgroups of 8 waves, each wave running the engine's
+    8-MFMA step on constant random operands (mode 0), on operand bits that change
+    every step in registers (mode 1), on random bf16 fragments read from LDS in
+    the engine's pattern (mode 2) and on constant operands of few set bits
+    (mode 3).  For each mode: the launch time (HIP events), the
+    shader clock the launch ran at (per-workgroup s_memtime cycles over
+    s_memrealtime 100 MHz ticks) and the MFMA TFLOP/s.  Prints one JSON line."""
+    import torch
+
+    from chunked_top_kl_head_amd import build as hip_build
+
+    path = hip_build.PROBE_LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.kd_probe_mfma_launch.restype = ctypes.c_int
+    lib.kd_probe_mfma_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    wgs, iters = 256, 200000
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    cycles = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    flop = wgs * 8 * iters * 8 * 32768.0
+    names = {0: "constant random operands", 1: "operands changing every step (registers)",
+             2: "random bf16 operands from LDS", 3: "constant operands of few set bits"}
+    modes = []
+    for mode in (0, 1, 2, 3):
+        runs = []
+        for rep in range(max(1, args.warmup) + max(1, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.kd_probe_mfma_launch(mode, wgs, iters, ctypes.c_void_p(sink.data_ptr()),
+                                          ctypes.c_void_p(cycles.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"kd_probe_mfma_launch failed: hipError {rc}")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep < max(1, args.warmup):
+                continue
+            ms = e0.elapsed_time(e1)
+            c = cycles.view(wgs, 2).double().sum(dim=0).tolist()
+            ghz = c[0] / c[1] * 0.1
+            runs.append((ms, flop / (ms * 1e-3) / 1e12, ghz))
+            print(f"mode {mode}: {ms:.2f} ms {runs[-1][1]:.1f} TFLOP/s at {ghz:.3f} GHz", file=sys.stderr, flush=True)
+        ms = sorted(r[0] for r in runs)[len(runs) // 2]
+        best = min(runs, key=lambda r: abs(r[0] - ms))
+        modes.append({"mode": mode, "operands": names[mode], "ms": round(best[0], 3),
+                      "tflops": round(best[1], 1), "clock_ghz": round(best[2], 3),
+                      "frac_of_nominal": round(best[1] / PEAK_BF16_TFLOPS, 4),
+                      "busy_at_clock": round(best[1] / (PEAK_BF16_TFLOPS * best[2] / 2.4), 4)})
+    out = {"metric": "sustained bf16 MFMA rate, no memory traffic", "unit": "TFLOP/s", "n_gpus": 1,
+           "peak_nominal": PEAK_BF16_TFLOPS, "nominal_clock_ghz": 2.4,
+           "config": {"workload": f"mfma_ceiling: {wgs} workgroups x 8 waves, {iters} steps of 8 "
+                                  "v_mfma_f32_32x32x16_bf16 per wave"},
+           "modes": modes}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def bench_teacher(args) -> int:
     """The cache producer from hidden states (kd_teacher_topk) with the
     workload's H [T, d] and W [V, d] standing in for the teacher's: per chunk a
@@ -219,6 +281,9 @@ def main() -> int:
     ap.add_argument("--teacher", action="store_true",
                     help="benchmark the cache producer from hidden states (kd_teacher_topk): the workload's "
                          "H and W as the teacher's, K = 100")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="measure the part's sustained bf16 MFMA rate and clock with no memory traffic "
+                         "(constant, changing and LDS-fed random operands)")
     ap.add_argument("--copy-calibration-bytes", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many bytes (a kernel of known "
                          "traffic, used to scale the FETCH_SIZE/WRITE_SIZE counters of a profiling run)")
@@ -242,6 +307,8 @@ def main() -> int:
         return bench_select(args)
     if args.teacher:
         return bench_teacher(args)
+    if args.mfma_ceiling:
+        return bench_mfma_ceiling(args)
     wl = synth.WORKLOADS[args.workload]
     chunk = args.chunk or wl.chunk
     t_gen = time.perf_counter()

@@ -1,4 +1,5 @@
-"""Build the HIP library ``libkdtopk.so`` for gfx950 with hipcc (in-tree)."""
+"""Build the HIP library ``libkdtopk.so`` for gfx950 with hipcc (in-tree), and
+the MFMA-rate probe ``libkdprobe.so`` that ``bench.py --mfma-ceiling`` runs."""
 from __future__ import annotations
 
 import os
@@ -9,6 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "kd_topk_kl.hip")
 LIB = os.path.join(PKG, "libkdtopk.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "kd_mfma_ceiling.hip")
+PROBE_LIB = os.path.join(PKG, "libkdprobe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -24,11 +27,11 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(src: str, lib: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           "-o", tmp, SRC]
+           "-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,8 +40,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the loss library and the MFMA-rate probe; returns the loss library's path."""
+    _hipcc(PROBE_SRC, PROBE_LIB, verbose)
+    return _hipcc(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -368,3 +368,24 @@ def test_teacher_argument_errors(lib):
     assert lib.kd_teacher_topk(ctypes.byref(p), P16, P16b, P4, P4, P16, n - 1, None) == B.KD_ERR_WORKSPACE
     # no positions: nothing to do, nothing dereferenced
     assert lib.kd_teacher_topk(ctypes.byref(teacher(T=0)), None, None, None, None, None, 0, None) == B.KD_OK
+
+
+def test_mfma_probe_library_loads_and_checks_arguments():
+    """The MFMA-rate probe that bench.py --mfma-ceiling runs: built beside the
+    library, exports its launcher, and rejects bad arguments before any launch."""
+    from chunked_top_kl_head_amd import build as hip_build
+
+    assert os.path.exists(hip_build.PROBE_LIB), "libkdprobe.so is not built"
+    probe = ctypes.CDLL(hip_build.PROBE_LIB)
+    f = probe.kd_probe_mfma_launch
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    buf = ctypes.c_void_p(16)   # never dereferenced: every call below is rejected first
+    invalid = 1                 # hipErrorInvalidValue
+    assert f(4, 256, 1000, buf, buf, None) == invalid      # unknown mode
+    assert f(-1, 256, 1000, buf, buf, None) == invalid
+    assert f(2, 0, 1000, buf, buf, None) == invalid        # no workgroups
+    assert f(2, 256, 1001, buf, buf, None) == invalid      # odd step count
+    assert f(0, 256, 0, buf, buf, None) == invalid
+    assert f(1, 256, 1000, None, buf, None) == invalid     # missing buffers
+    assert f(1, 256, 1000, buf, None, None) == invalid
