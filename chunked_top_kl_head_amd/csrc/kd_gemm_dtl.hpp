@@ -314,11 +314,27 @@ __device__ __forceinline__ void wave_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// LDS of the engine: kDtlStages pipeline stages of kDtlStage bytes (A tile,
-// then B tile).
+// LDS of the engine's two schedules.
+//
+// Two-stage (RING = false): kDtlStages pipeline stages of kDtlStage bytes (A
+// tile, then B tile); every load of a step has one step to land.
+//
+// Operand ring (RING = true): the A tiles of kDtlSlotsA consecutive steps, then
+// the B tiles of kDtlSlotsB, one tile per slot (160 KiB with 3 + 2).  A tiles
+// are loaded two steps ahead of their use, spread over the MFMAs of the
+// preceding step's first SUB - 1 sub-steps; B tiles one step ahead, right after
+// the barrier that frees their slot.  The deeper prefetch pays where operand
+// slices come from HBM with little reuse and the contraction is latency-bound
+// (short chunks: fewer rows share each W tile); where the part runs at its
+// power limit (long chunks) the two-stage schedule is faster.
 constexpr int kDtlStage = 2 * kDtlTile;
 constexpr int kDtlLds = kDtlStages * kDtlStage;
 static_assert(kDtlLds >= 128 * 1024, "the epilogues stage through 128 KiB of LDS");
+constexpr int kDtlSlotsA = 3;
+constexpr int kDtlSlotsB = 2;
+constexpr int kDtlLdsRing = (kDtlSlotsA + kDtlSlotsB) * kDtlTile;
+static_assert(kDtlLdsRing <= 160 * 1024 && kDtlLdsRing >= kDtlLds, "the ring fits the LDS");
+template <bool RING> constexpr int dtl_lds_bytes() { return RING ? kDtlLdsRing : kDtlLds; }
 
 // s_waitcnt immediate (gfx9): vmcnt (6 bits, split), expcnt 7, lgkmcnt.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
@@ -344,16 +360,20 @@ template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
 // the groups of the following step before its barrier; they have NS - 2
 // further steps to land before the barrier that publishes step j.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool B_BLOCKED, class Epi>
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool B_BLOCKED, bool RING, class Epi>
 __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B, const GemmGeom& g,
                                               const typename Epi::Params& ep, lds_t* smem) {
     static_assert(BM == 256 && BN == 256, "tile shape");
     constexpr int BK = kDtlBK, NS = kDtlStages, SUB = kDtlSub;
+    // A and B slots: the two-stage schedule's stages, or the ring's 3 + 2
+    constexpr int SA = RING ? kDtlSlotsA : NS, SB = RING ? kDtlSlotsB : NS;
     using LA = DtlLoader<BM, A_KMAJOR>;
     using LB = DtlLoader<BN, B_KMAJOR, B_BLOCKED>;
     using Mma = DtlMma<BM, BN>;
     constexpr int FM = Mma::FM, FN = Mma::FN, WN = Mma::WN;
-    constexpr int NT = LA::NI + LB::NI;          // load instructions per step and loader wave
+    constexpr int NA = LA::NI, NB = LB::NI;      // load instructions per step and loader wave
+    constexpr int NT = NA + NB;
+    static_assert(!RING || 2 * NT <= 63, "vmcnt range");
     // two stages: every load rides on the group right after the barrier (the
     // earliest its stage is free; measured best); more stages: half and half
     constexpr int kPost = NS == 2 ? NT : NT / 2;
@@ -392,32 +412,35 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
 #pragma unroll
             for (int e = 0; e < 16; ++e) mma.acc[i][j][e] = 0.f;
 
-    // LDS layout: the A tile of stage s at s * kDtlTile, its B tile at
-    // (NS + s) * kDtlTile.  The B fragment offsets carry the NS * kDtlTile, so
-    // both operands of stage s are read from the base s * kDtlTile plus a
-    // per-lane offset and a constant below 64 KiB: with the stage known at
-    // compile time (the main loop is unrolled NS times) the constant is the
-    // LDS instruction's immediate offset and no address is recomputed per step.
+    // LDS layout: A slot s at s * kDtlTile, B slot s at (SA + s) * kDtlTile
+    // (two-stage: stage s holds A slot s and B slot s).  The B fragment offsets
+    // carry the SA * kDtlTile, so both operands are read from a slot base plus
+    // a per-lane offset and a constant: with the slots known at compile time
+    // (the main loop is unrolled over the slots' period) the constants become
+    // the LDS instructions' immediate offsets and no address is recomputed per
+    // step.
     typename LA::Frag fa = LA::frag_addr(wm * (BM / 2), lane);
     typename LB::Frag fb = LB::frag_addr(wn * (BN / WN), lane);
 #pragma unroll
-    for (int y = 0; y < (int)(sizeof(fb.off) / sizeof(int)); ++y) fb.off[y] += NS * kDtlTile;
+    for (int y = 0; y < (int)(sizeof(fb.off) / sizeof(int)); ++y) fb.off[y] += SA * kDtlTile;
     struct Frags {
         u32x4 a[FM], b[FN];
     };
-    auto a_tile = [&](int step) { return smem + (int)((unsigned)step % (unsigned)NS) * kDtlTile; };
-    auto b_tile = [&](int step) { return smem + (NS + (int)((unsigned)step % (unsigned)NS)) * kDtlTile; };
+    auto a_tile = [&](int step) { return smem + (int)((unsigned)step % (unsigned)SA) * kDtlTile; };
+    auto b_tile = [&](int step) { return smem + (SA + (int)((unsigned)step % (unsigned)SB)) * kDtlTile; };
     // FMV: fragments of this wave's rows that hold output rows below M (the
-    // others are neither read nor multiplied); ps: the stage (a constant in the
-    // unrolled main loop)
-    auto read = [&](Frags& f, int ps, int s, auto fmv_c) {
+    // others are neither read nor multiplied); sa, sb: the step's A and B slots
+    // (constants in the unrolled main loop; the B fragment offsets already
+    // carry the A slots' extent)
+    auto read = [&](Frags& f, int sa, int sb, int s, auto fmv_c) {
         constexpr int FMV = decltype(fmv_c)::value;
         if constexpr (FMV == 0) return;
-        const lds_t* base = smem + ps * kDtlTile;
+        const lds_t* base_a = smem + sa * kDtlTile;
+        const lds_t* base_b = smem + sb * kDtlTile;
 #pragma unroll
-        for (int i = 0; i < FMV; ++i) f.a[i] = LA::frag(base, fa, i, s);
+        for (int i = 0; i < FMV; ++i) f.a[i] = LA::frag(base_a, fa, i, s);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) f.b[j] = LB::frag(base, fb, j, s);
+        for (int j = 0; j < FN; ++j) f.b[j] = LB::frag(base_b, fb, j, s);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto mfma1 = [&](const Frags& f, int q) {
@@ -446,8 +469,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     // needs the K-tail check (compile-time, so the checks vanish)
     auto load1 = [&](const Pending& p, int q, auto WHOLE) {
         const bool full = decltype(WHOLE)::value || p.full;
-        if (q < LA::NI) la.issue1(p.ra, p.tile, q, p.k0, kend, full, wave);
-        else            lb.issue1(p.rb, p.tileb, q - LA::NI, p.k0, kend, full, wave);
+        if (q < NA) la.issue1(p.ra, p.tile, q, p.k0, kend, full, wave);
+        else        lb.issue1(p.rb, p.tileb, q - NA, p.k0, kend, full, wave);
     };
     // one MFMA group carrying load instructions first .. first + CNT - 1
     auto group = [&](const Frags& f, auto with_loads, const Pending& p, auto first_c, auto cnt_c, auto fmv_c,
@@ -478,8 +501,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
     };
     using Z = std::integral_constant<int, 0>;
 
-    // Main loop of one wave; LOADS: this wave issues loads.
-    auto run = [&](auto LOADS, auto FMVc, auto WHOLE) {
+    // Main loop of one wave, two-stage schedule; LOADS: this wave issues loads.
+    auto run2 = [&](auto LOADS, auto FMVc, auto WHOLE) {
         constexpr bool loads = decltype(LOADS)::value;
         Frags f0, f1;
         if constexpr (loads) {
@@ -503,7 +526,7 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
             }
         }
         wave_barrier();
-        read(f0, 0, 0, FMVc);
+        read(f0, 0, 0, 0, FMVc);
         // One K step.  PRE / POST: the groups before / after this step's
         // barrier carry loads of step it + NS - 1 / it + NS (compile-time, so
         // the MFMA groups stay free of branches); ps = it mod NS.
@@ -527,10 +550,10 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                 using First = std::integral_constant<int, lo>;
                 using Cnt = std::integral_constant<int, hi - lo>;
                 if constexpr (s % 2 == 0) {
-                    read(f1, ps, s + 1, FMVc);
+                    read(f1, ps, ps, s + 1, FMVc);
                     group(f0, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
                 } else {
-                    read(f0, ps, s + 1, FMVc);
+                    read(f0, ps, ps, s + 1, FMVc);
                     group(f1, std::integral_constant<bool, pre>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
                 }
             });
@@ -540,7 +563,8 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
                 if constexpr (decltype(PRE)::value) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kAhead, 0));
                 else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
                 wave_barrier();                       // every wave's loads landed; stage ps is free
-                read(f0, ps + 1 == NS ? 0 : ps + 1, 0, FMVc);
+                const int pn = ps + 1 == NS ? 0 : ps + 1;
+                read(f0, pn, pn, 0, FMVc);
             }
             if constexpr (post) pq = pending_for(it + NS);
             // sub-step SUB - 1
@@ -558,6 +582,90 @@ __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B
             ++it;
         }
         for (; it < nk; ++it) body(no, no, it, stage_of(it));
+    };
+
+    // Main loop of one wave, operand ring: step j's A tile in A slot j mod SA,
+    // its B tile in B slot j mod SB.  The barrier inside step it (after its
+    // last fragment reads) frees step it's slots.  The loader waves issue
+    // A(it + 2) over the MFMAs of step it's first SUB - 1 sub-steps (its slot
+    // was freed by the previous barrier) and B(it + 2) over the last
+    // sub-step's, right after the barrier.  At the wait before the barrier of
+    // step it everything up to B(it + 1) has landed; only A(it + 2) may still
+    // be in flight.
+    auto runr = [&](auto LOADS, auto FMVc, auto WHOLE) {
+        constexpr bool loads = decltype(LOADS)::value;
+        Frags f0, f1;
+        if constexpr (loads) {
+            // steps 0 and 1 (A then B each), before the first barrier
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (j < nk) {
+                    const Pending p = pending_for(j);
+#pragma unroll
+                    for (int q = 0; q < NT; ++q) load1(p, q, WHOLE);
+                }
+            }
+            // step 0 landed (step 1's loads may be in flight)
+            if (1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_imm(NT, 15));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        }
+        wave_barrier();
+        read(f0, 0, 0, 0, FMVc);
+        // One K step.  LD: step it + 2 exists, so this step carries its loads
+        // (compile-time, so the MFMA groups stay free of branches); sa, sb:
+        // slots of step it.
+        auto body = [&](auto LD, int it, int sa, int sb) {
+            la.hide();
+            lb.hide();
+#pragma unroll
+            for (int y = 0; y < (int)(sizeof(fa.off) / sizeof(int)); ++y) opaque(fa.off[y]);
+#pragma unroll
+            for (int y = 0; y < (int)(sizeof(fb.off) / sizeof(int)); ++y) opaque(fb.off[y]);
+            constexpr bool ld = decltype(LD)::value && loads;
+            Pending pp{};
+            if constexpr (ld) pp = pending_for(it + 2);
+            // sub-steps 0 .. SUB - 2: read the next sub-step's fragments, then
+            // this one's MFMAs with a share of A(it + 2)'s loads
+            static_for<SUB - 1>([&](auto S) {
+                constexpr int s = decltype(S)::value;
+                using First = std::integral_constant<int, (s * NA) / (SUB - 1)>;
+                using Cnt = std::integral_constant<int, ((s + 1) * NA) / (SUB - 1) - (s * NA) / (SUB - 1)>;
+                if constexpr (s % 2 == 0) {
+                    read(f1, sa, sb, s + 1, FMVc);
+                    group(f0, std::integral_constant<bool, ld>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
+                } else {
+                    read(f0, sa, sb, s + 1, FMVc);
+                    group(f1, std::integral_constant<bool, ld>{}, pp, First{}, Cnt{}, FMVc, WHOLE);
+                }
+            });
+            static_assert(SUB % 2 == 0, "the last sub-step uses the second register set");
+            if (it + 1 < nk) {
+                // this wave's loads of step it + 1 and its reads of step it are
+                // complete (A(it + 2) may still be in flight)
+                if constexpr (decltype(LD)::value) __builtin_amdgcn_s_waitcnt(waitcnt_imm(NA, 0));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+                wave_barrier();                       // every wave's loads landed; step it's slots are free
+                read(f0, sa + 1 == SA ? 0 : sa + 1, sb + 1 == SB ? 0 : sb + 1, 0, FMVc);
+            }
+            // sub-step SUB - 1 with B(it + 2)'s loads (its slot was freed just now)
+            group(f1, std::integral_constant<bool, ld>{}, pp, std::integral_constant<int, NA>{},
+                  std::integral_constant<int, NB>{}, FMVc, WHOLE);
+        };
+        const std::true_type yes{};
+        const std::false_type no{};
+        constexpr int P = SA * SB;   // both slot indices repeat every SA * SB steps
+        int it = 0;
+        for (; it + P + 1 < nk; it += P)
+            static_for<P>([&](auto Q) {
+                constexpr int q = decltype(Q)::value;
+                body(yes, it + q, q % SA, q % SB);
+            });
+        for (; it + 2 < nk; ++it) body(yes, it, it % SA, it % SB);
+        for (; it < nk; ++it) body(no, it, it % SA, it % SB);
+    };
+    auto run = [&](auto LOADS, auto FMVc, auto WHOLE) {
+        if constexpr (RING) runr(LOADS, FMVc, WHOLE);
+        else run2(LOADS, FMVc, WHOLE);
     };
     if (nk > 0) {
         // rows of this wave's half below M: all (4 fragments), at most 64 (2)

@@ -442,9 +442,15 @@ template <typename E, int BM, int BN> struct GradWEpi {
             // Two passes over halves of 128 hidden indices (owned by the waves
             // with wm = half): the half tile goes to LDS as [v][128] fp32
             // (16-byte chunk c of row v at c ^ (v & 31)), then every wave
-            // updates whole 512-byte row segments of grad_W.
-            const int wave = tid >> 6;
-            const int c = lane & 31;
+            // updates whole 512-byte row segments of grad_W.  The thread index
+            // goes through an empty asm first, so that none of the addresses
+            // below is computed ahead of the main loop (where they would hold
+            // registers the whole time).
+            int tid_o = tid;
+            opaque(tid_o);
+            const int wave = tid_o >> 6;
+            const int lane_o = tid_o & 63;
+            const int c = lane_o & 31;
             constexpr int RW = 256 / kDtlWaves;   // staged rows per wave
             constexpr int NK = RW / 2;            // 16-byte pieces per thread and half
             // this thread's pieces of grad_W: the first half's are read before
@@ -462,7 +468,7 @@ template <typename E, int BM, int BN> struct GradWEpi {
             const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.gw + (int64_t)n0 * p.d,
                                                         p.accumulate ? (uint32_t)rows * (uint32_t)p.d * 4u : 0u);
             auto off_of = [&](int half, int k) -> uint32_t {
-                const int vl = wave * RW + 2 * k + (lane >> 5);
+                const int vl = wave * RW + 2 * k + (lane_o >> 5);
                 const int h = m0 + 128 * half + 4 * c;
                 return h < p.d ? ((uint32_t)vl * (uint32_t)p.d + (uint32_t)h) * 4u : kOOB;
             };
@@ -494,7 +500,7 @@ template <typename E, int BM, int BN> struct GradWEpi {
                 __syncthreads();
 #pragma unroll
                 for (int k = 0; k < NK; ++k) {
-                    const int vl = wave * RW + 2 * k + (lane >> 5);
+                    const int vl = wave * RW + 2 * k + (lane_o >> 5);
                     const f32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
                         smem + vl * 512 + ((c ^ (vl & 31)) << 4));
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val + old[k]), rw,

@@ -48,23 +48,43 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Operand A, Operand B, Ge
 }
 
 // bf16 operands: direct-to-LDS engine (8 waves, 32x32x16 bf16 MFMA); BB: B is
-// the chunk's G in its blocked layout
-template <bool AK, bool BK, bool BB, class Epi>
+// the chunk's G in its blocked layout; RING: the operand-ring schedule (A tiles
+// two steps ahead) instead of the two-stage one
+template <bool AK, bool BK, bool BB, bool RING, class Epi>
 __global__ __launch_bounds__(kDtlThreads) void gemm_kernel_dtl(Operand A, Operand B, GemmGeom g,
                                                                typename Epi::Params ep) {
-    __shared__ __attribute__((aligned(1024))) char smem[kDtlLds];
-    gemm_body_dtl<BM, BN, AK, BK, BB, Epi>(A, B, g, ep, (lds_t*)smem);
+    __shared__ __attribute__((aligned(1024))) char smem[dtl_lds_bytes<RING>()];
+    gemm_body_dtl<BM, BN, AK, BK, BB, RING, Epi>(A, B, g, ep, (lds_t*)smem);
 }
 
+// Chunks of at most this many rows run their contractions on the operand ring
+// (the bf16 engine's deeper prefetch): with few rows per chunk each W tile is
+// shared by few output tiles and its slices come from HBM, and the two-stage
+// schedule leaves the matrix cores waiting for them.  Measured on the
+// GPT-OSS-like shapes (d = 2880, V = 201088): the ring is faster for the
+// logits and grad_H contractions at 1,024-4,096 rows and for grad_W at
+// 1,024-2,048, slower for all three at 8,192 rows, where the part runs at its
+// power limit.
+constexpr int64_t kRingRows = 4096;        // logits (loss and teacher) and grad_H
+constexpr int64_t kRingRowsGradW = 2048;   // grad_W
+
 // Launch of one contraction on the engine that matches the element type.
-// BB: B is the chunk's G (blocked in the bf16 layout, row-major for fp32).
+// BB: B is the chunk's G (blocked in the bf16 layout, row-major for fp32);
+// ring: the bf16 engine's schedule (ignored by the fp32 engine).
 template <typename E, bool AK, bool BK, bool BB, class Epi>
 static void launch_gemm(dim3 grid, hipStream_t stream, const Operand& A, const Operand& B, const GemmGeom& g,
-                        const typename Epi::Params& ep) {
-    if constexpr (Elem<E>::size == 2)
-        hipLaunchKernelGGL((gemm_kernel_dtl<AK, BK, BB, Epi>), grid, dim3(kDtlThreads), 0, stream, A, B, g, ep);
-    else
+                        const typename Epi::Params& ep, bool ring) {
+    if constexpr (Elem<E>::size == 2) {
+        if (ring)
+            hipLaunchKernelGGL((gemm_kernel_dtl<AK, BK, BB, true, Epi>), grid, dim3(kDtlThreads), 0, stream, A, B, g,
+                               ep);
+        else
+            hipLaunchKernelGGL((gemm_kernel_dtl<AK, BK, BB, false, Epi>), grid, dim3(kDtlThreads), 0, stream, A, B,
+                               g, ep);
+    } else {
+        (void)ring;
         hipLaunchKernelGGL((gemm_kernel<E, AK, BK, Epi>), grid, dim3(kThreads), 0, stream, A, B, g, ep);
+    }
 }
 
 struct Plan {
@@ -292,12 +312,13 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             lp.ignore = ignore ? ignore + t0 : nullptr;
             lp.ref = ref;
             const dim3 grid = gemm_grid(g, 1);
+            const bool ring = rc <= kRingRows;
             if (op == KD_OP_FORWARD)
-                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kStats>>(grid, stream, A, B, g, lp);
+                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kStats>>(grid, stream, A, B, g, lp, ring);
             else if (fused)
-                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kFused>>(grid, stream, A, B, g, lp);
+                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kFused>>(grid, stream, A, B, g, lp, ring);
             else
-                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kBwd>>(grid, stream, A, B, g, lp);
+                launch_gemm<E, true, true, false, LogitsEpi<E, BM, BN, kBwd>>(grid, stream, A, B, g, lp, ring);
         }
         // ---- row kernel
         {
@@ -337,7 +358,8 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             hp.fscale = fused ? fscale : nullptr;
             {
                 StageScope scope(KD_STAGE_GRAD_H, stream);
-                launch_gemm<E, false, true, true, GradHEpi<E, BM, BN>>(gemm_grid(g, pl.splits), stream, A, B, g, hp);
+                launch_gemm<E, false, true, true, GradHEpi<E, BM, BN>>(gemm_grid(g, pl.splits), stream, A, B, g, hp,
+                                                                       rc <= kRingRows);
             }
             if (pl.splits > 1) {
                 const int64_t n4 = rc * pl.d / 4;
@@ -355,7 +377,8 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 8);
             GradWParams wp{};
             wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0 || pl.accumulate;
-            launch_gemm<E, false, false, true, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp);
+            launch_gemm<E, false, false, true, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp,
+                                                                    rc <= kRingRowsGradW);
         }
     }
     if (want_loss) hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, stream, hdr, loss);
@@ -424,7 +447,8 @@ static kd_status run_teacher(const TeacherPlan& pl, const void* H, const void* W
         RawLogitsParams rp{};
         rp.out = z; rp.ld = pl.ld; rp.V = (int)pl.V; rp.rows = (int)rc;
         rp.bmax = pl.blocks ? bmax : nullptr; rp.nblk = (int)pl.nblk;
-        launch_gemm<E, true, true, false, RawLogitsEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, rp);
+        launch_gemm<E, true, true, false, RawLogitsEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, rp,
+                                                                   rc <= kRingRows);
         if (pl.blocks)
             hipLaunchKernelGGL(topk_select_blocks_kernel, dim3((unsigned)rc), dim3(kSelThreads), 0, stream, z, pl.ld,
                                (int)pl.V, (int)pl.K, bmax, (int)pl.nblk, idx + t0 * pl.K, val + t0 * pl.K);
