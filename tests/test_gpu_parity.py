@@ -117,6 +117,35 @@ def test_small_parity(oracle, name):
     diagnostics(ref, out["fused"], x, tau)
 
 
+# The bf16 engine runs a chunk's contractions on one of two schedules, chosen
+# by the chunk's rows (the operand ring up to 4,096 rows for the logits and
+# grad_H contractions and up to 2,048 for grad_W, the two-stage pipeline
+# above).  These chunk sizes cross both switch points on small shapes with
+# tails, so both schedules of every contraction meet the oracle:
+#   4,608 rows: all three on the two-stage schedule, the ragged 92-row
+#               remainder on the ring;
+#   3,000 rows: logits and grad_H on the ring, grad_W on the two-stage one.
+SWITCH_CASES = {
+    # name: (T, d, V, K, tau, mask, chunk, seed)
+    "two_stage_all_ktail": (4700, 136, 3001, 30, 1.5, ("random", 0.1), 4608, 105),
+    "ring_lh_two_stage_w_mtail": (3100, 320, 3001, 30, 1.0, ("random", 0.05), 3000, 106),
+}
+
+
+@pytest.mark.parametrize("name", list(SWITCH_CASES))
+def test_both_engine_schedules(name):
+    from oracle import kd_oracle_blas
+
+    T, d, V, K, tau, mask, chunk, seed = SWITCH_CASES[name]
+    say(f"case {name}: T={T} d={d} V={V} K={K} tau={tau} bf16 chunk={chunk}")
+    x = synth.make_inputs(T, d, V, K, tau=tau, dtype="bf16", seed=seed, mask=mask)
+    out = run_all_paths(upload(x), tau, chunk)
+    ref = kd_oracle_blas.full(x.H, x.W, x.topk_idx, x.topk_logit, x.ignore, tau=tau)
+    for path in ("fused", "split"):
+        check_against(ref, out[path], tol_for("bf16"), x, path)
+    diagnostics(ref, out["fused"], x, tau)
+
+
 def test_tiny_workload(oracle):
     """The smallest standard workload in full: fp32, T=256, d=256, V=4096, K=16, chunk 64."""
     w = synth.WORKLOADS["tiny"]

@@ -131,6 +131,7 @@ def check_teacher(H64, W64, idx, val, K):
     ("bf16", 200, 136, 20000, 100, 64),    # K close to the number of blocks (157)
     ("bf16", 70, 136, 3001, 100, 0),       # V not a multiple of 4 (padded rows of the chunk buffer); K > blocks
     ("bf16", 33, 64, 37, 37, 16),          # K = V
+    ("bf16", 4700, 136, 3001, 20, 4608),   # a chunk above 4,096 rows: the two-stage schedule, then the ring
     ("f32", 130, 64, 3000, 10, 64),
     ("f32", 100, 64, 1000, 10, 64),
 ])
