@@ -16,8 +16,10 @@
 //     (512-byte k-rows, 16-byte chunks XOR-swizzled by k); fragments are two
 //     ds_read_b64_tr_b16 per lane, which transpose 4 x 16 blocks across the
 //     16 lanes of a quarter-wave.
-// Two LDS stages of one 64-deep K step each: one is consumed while the loads of
-// the other are in flight (see the main loop below).
+// Two schedules (a template switch, chosen per launch by the host): two LDS
+// stages of one 64-deep K step each, one consumed while the loads of the other
+// are in flight; or an operand ring of three A and two B tiles in the whole
+// 160 KiB, which loads A tiles two steps ahead (see the main loops below).
 #pragma once
 
 #include <type_traits>
@@ -353,12 +355,13 @@ template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
 // the barrier that publishes the next stage, so they cover the latency of the
 // next stage's first fragment reads.
 //
-// Stages form a ring: step j lives in stage j mod NS.  The stage of step it is
+// Two-stage schedule: step j lives in stage j mod NS.  The stage of step it is
 // free once every wave has passed the barrier that ends step it's reads, so
 // the loads of step j are issued partly on the MFMA group after the barrier
 // that frees its stage (kPost instructions per loader wave) and the rest on
 // the groups of the following step before its barrier; they have NS - 2
-// further steps to land before the barrier that publishes step j.
+// further steps to land before the barrier that publishes step j.  The
+// operand ring (RING) is described at its main loop.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, bool B_BLOCKED, bool RING, class Epi>
 __device__ __forceinline__ void gemm_body_dtl(const Operand& A, const Operand& B, const GemmGeom& g,
