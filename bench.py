@@ -34,11 +34,41 @@ KERNEL_SOURCES = ("kd_common.hpp", "kd_gemm.hpp", "kd_gemm_dtl.hpp", "kd_kernels
                   "kd_topk_kl.hip")
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed (string and
+    character literals kept), so that comment edits leave the hash alone."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_hash(sources: dict | None = None) -> str:
+    """Hash of the kernel sources' code (comments and whitespace excluded);
+    ``sources`` maps file name to text (default: the files in csrc/)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "chunked_top_kl_head_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        if sources is None:
+            with open(os.path.join(ROOT, "chunked_top_kl_head_amd", "csrc", f), encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = sources[f]
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 
