@@ -3,7 +3,8 @@
 * A 201,088-token vocabulary with chunks of 8,192 positions: one chunk's G is
   8,192 x 201,216 bf16 = 3.3 GB, so the operand windows of both gradient
   contractions lie beyond 2^31 bytes (ids from 131,072 on sit at G offsets
-  past 2 GiB).  T = 8,300 leaves a ragged second chunk of 108 rows; d = 136
+  past 2 GiB).  Two wider vocabularies (300,000 with 4,096-row chunks,
+  600,000 with 2,048) do the same on the engine's operand-ring schedule.  T = 8,300 leaves a ragged second chunk of 108 rows; d = 136
   puts a K tail inside the logits contraction's last step and d = 320 a
   partial hidden tile in both gradient contractions.  Fused and split entries
   are compared with the fp64 oracle in full (loss, lse, row losses, grad_H,
@@ -39,9 +40,14 @@ def say(*a):
 
 
 # name: (T, d, V, K, tau, mask, chunk, seed)
+# 8,192-row chunks run every contraction on the engine's two-stage schedule;
+# the wide-vocabulary cases put G beyond 2 GiB in chunks short enough for the
+# operand ring (logits and grad_H up to 4,096 rows, grad_W up to 2,048).
 WIDE_CASES = {
     "d136_ktail_mask": (8300, 136, 201088, 100, 1.0, ("random", 0.05), 8192, 121),
     "d320_mtail_tau2": (8300, 320, 201088, 100, 2.0, None, 8192, 122),
+    "ring_lh_V300k": (4200, 64, 300000, 20, 1.0, ("random", 0.05), 4096, 123),
+    "ring_all_V600k": (2100, 64, 600000, 20, 1.0, None, 2048, 124),
 }
 
 
@@ -57,11 +63,14 @@ def test_chunk_G_beyond_2GiB(name):
     for path in ("fused", "split"):
         check_against(ref, out[path], tol_for("bf16"), x, path)
     diagnostics(ref, out["fused"], x, tau)
-    # ids whose G entries sit beyond 2 GiB of the chunk buffer, on their own
-    far = np.arange(131072, V)
+    # ids whose G entries sit beyond 2 GiB of the blocked chunk buffer (element
+    # (r, v) at ((v / 64) C + r) 64 + v % 64, two bytes each), on their own
+    first_far = (1 << 30) // chunk
+    assert first_far < V
+    far = np.arange(first_far, V)
     for path in ("fused", "split"):
         e = np.max(np.abs(out[path]["grad_W"][far] - ref["grad_W"][far])) / np.max(np.abs(ref["grad_W"][far]))
-        say(f"  {path}: grad_W rows of ids >= 131072, at their own scale: {e:.2e}")
+        say(f"  {path}: grad_W rows of ids >= {first_far}, at their own scale: {e:.2e}")
         assert e <= 2e-2
     del out, ref
     gc.collect()
