@@ -146,6 +146,41 @@ def test_both_engine_schedules(name):
     diagnostics(ref, out["fused"], x, tau)
 
 
+def _random_cases(n=10, seed=2026):
+    """Seeded random shapes: hidden sizes 8..520 (K tails inside a step, partial
+    hidden tiles), vocabularies that are not multiples of 4, chunks from one row
+    to all rows, temperatures 0.5..3, random masks; bf16 and fp32."""
+    rng = np.random.default_rng(seed)
+    cases = {}
+    for i in range(n):
+        dt = "f32" if i % 4 == 3 else "bf16"
+        T = int(rng.integers(1, 900))
+        d = 8 * int(rng.integers(1, 66))
+        V = int(rng.integers(40, 9000))
+        K = int(rng.integers(1, min(200, V) + 1))
+        chunk = 0 if i % 5 == 0 else int(rng.integers(1, T + 1))
+        tau = round(float(rng.uniform(0.5, 3.0)), 3)
+        mask = None if i % 3 == 0 else ("random", round(float(rng.uniform(0.0, 0.3)), 3))
+        cases[f"r{i}_{dt}_T{T}_d{d}_V{V}_K{K}_c{chunk}"] = (T, d, V, K, tau, dt, mask, chunk, 200 + i)
+    return cases
+
+
+RANDOM_CASES = _random_cases()
+
+
+@pytest.mark.parametrize("name", list(RANDOM_CASES))
+def test_random_shapes(name):
+    from oracle import kd_oracle_blas
+
+    T, d, V, K, tau, dt, mask, chunk, seed = RANDOM_CASES[name]
+    say(f"case {name}: tau={tau} mask={mask}")
+    x = synth.make_inputs(T, d, V, K, tau=tau, dtype=dt, seed=seed, mask=mask)
+    out = run_all_paths(upload(x), tau, chunk)
+    ref = kd_oracle_blas.full(x.H, x.W, x.topk_idx, x.topk_logit, x.ignore, tau=tau)
+    for path in ("fused", "split"):
+        check_against(ref, out[path], tol_for(dt), x, path)
+
+
 def test_tiny_workload(oracle):
     """The smallest standard workload in full: fp32, T=256, d=256, V=4096, K=16, chunk 64."""
     w = synth.WORKLOADS["tiny"]
