@@ -165,7 +165,25 @@ def _random_cases(n=10, seed=2026):
     return cases
 
 
-RANDOM_CASES = _random_cases()
+def _random_medium_cases(n=4, seed=2027):
+    """Seeded random problems whose chunks (2,049 rows up to all of T) put grad_W,
+    and above 4,096 rows the logits and grad_H contractions too, on the engine's
+    two-stage schedule, with random hidden and vocabulary tails."""
+    rng = np.random.default_rng(seed)
+    cases = {}
+    for i in range(n):
+        T = int(rng.integers(4100, 5200))
+        d = 8 * int(rng.integers(1, 48))
+        V = int(rng.integers(300, 6000))
+        K = int(rng.integers(1, min(120, V) + 1))
+        chunk = int(rng.integers(2049, T + 1))
+        tau = round(float(rng.uniform(0.5, 3.0)), 3)
+        mask = ("random", round(float(rng.uniform(0.0, 0.2)), 3)) if i % 2 else None
+        cases[f"m{i}_bf16_T{T}_d{d}_V{V}_K{K}_c{chunk}"] = (T, d, V, K, tau, "bf16", mask, chunk, 300 + i)
+    return cases
+
+
+RANDOM_CASES = {**_random_cases(), **_random_medium_cases()}
 
 
 @pytest.mark.parametrize("name", list(RANDOM_CASES))
