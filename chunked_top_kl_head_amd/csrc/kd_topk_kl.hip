@@ -374,11 +374,13 @@ static kd_status run(const Plan& pl, kd_op op, const void* H, const void* W, con
             // fused entry: G = fscale_t * stored values, so the operand is fscale_t * H_t
             const Operand A = operand(fused ? static_cast<const char*>(Hs) : Hc, pl.d, rc * pl.d * es);
             const Operand B = g_operand(G, pl);
-            const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, 8);
+            // tiles grouped 8 deep in M (hidden); 12 on the operand ring, where
+            // each tile has few K steps (measured on 1,024-row chunks: -2.3%)
+            const bool ring = rc <= kRingRowsGradW;
+            const GemmGeom g = geom(pl.d, pl.V_pad, rc, 1, bk, ring ? 12 : 8);
             GradWParams wp{};
             wp.gw = grad_W; wp.d = (int)pl.d; wp.V = (int)pl.V; wp.accumulate = t0 > 0 || pl.accumulate;
-            launch_gemm<E, false, false, true, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp,
-                                                                    rc <= kRingRowsGradW);
+            launch_gemm<E, false, false, true, GradWEpi<E, BM, BN>>(gemm_grid(g, 1), stream, A, B, g, wp, ring);
         }
     }
     if (want_loss) hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, stream, hdr, loss);
