@@ -146,6 +146,30 @@ def test_both_engine_schedules(name):
     diagnostics(ref, out["fused"], x, tau)
 
 
+def test_schedules_agree_bitwise_on_logits():
+    """Both schedules accumulate the K steps of a tile in the same order, so a
+    row's logits, hence its lse and row loss, are the same bits whichever
+    schedule its chunk ran on: 4,608-row chunks (two-stage) against 1,024-row
+    chunks (operand ring).  The two-stage run is also repeated bitwise."""
+    T, d, V, K, tau, mask, _, seed = SWITCH_CASES["two_stage_all_ktail"]
+    x = synth.make_inputs(T, d, V, K, tau=tau, dtype="bf16", seed=seed, mask=mask)
+    dev = upload(x)
+
+    def run(chunk):
+        loss, gH, gW, lse, rl = B.kd_topk_kl_fused(dev["H"], dev["W"], dev["topk_idx"], dev["topk_logit"],
+                                                   dev["ignore"], temperature=tau, chunk=chunk, want_lse=True,
+                                                   want_row_loss=True)
+        torch.cuda.synchronize()
+        return loss.clone(), gH.clone(), gW.clone(), lse.clone(), rl.clone()
+
+    a, b, c = run(4608), run(4608), run(1024)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v), "two-stage schedule not run-to-run deterministic"
+    assert torch.equal(a[3].view(torch.int32), c[3].view(torch.int32)), "lse differs between schedules"
+    assert torch.equal(a[4].view(torch.int32), c[4].view(torch.int32)), "row losses differ between schedules"
+    say("  lse and row losses bitwise equal across schedules; two-stage repeat bitwise equal")
+
+
 def _random_cases(n=10, seed=2026):
     """Seeded random shapes: hidden sizes 8..520 (K tails inside a step, partial
     hidden tiles), vocabularies that are not multiples of 4, chunks from one row
