@@ -339,7 +339,10 @@ template <typename E, int BM, int BN> struct RawLogitsEpi {
                     if (t >= p.rows) continue;
                     float* dst = p.out + (int64_t)t * p.ld + v0;
                     if (v0 + 3 < p.V) {
-                        *reinterpret_cast<f32x4*>(dst) = val;
+                        // streamed past the caches: the select reads a few
+                        // blocks of each row much later, and the lines would
+                        // only displace the contraction's operand slices
+                        __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(dst));
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
