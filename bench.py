@@ -293,6 +293,55 @@ def bench_teacher(args) -> int:
     return 0
 
 
+def bench_vendor_gemm(args) -> int:
+    """Yardstick for the engine's per-launch rates: the vendor BLAS (hipBLASLt,
+    through torch.matmul) on the three contraction shapes of one full chunk of
+    the workload, with bf16 outputs and no epilogue work (logits H_c W^T, grad_H
+    G_c W, grad_W G_c^T H_c).  Operands are seeded random bf16 of the workload's
+    scales.  Prints one JSON line."""
+    import torch
+
+    from chunked_top_kl_head_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    C = min(args.chunk or wl.chunk, wl.T)
+    d, V = wl.d, wl.V
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    W = (torch.randn(V, d, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    H = torch.randn(C, d, device=dev, generator=gen).to(torch.bfloat16)
+    G = (torch.randn(C, V, device=dev, generator=gen) * 1e-3).to(torch.bfloat16)
+    flop = 2.0 * C * d * V
+    cases = [("logits", lambda: torch.matmul(H, W.t())),
+             ("grad_H", lambda: torch.matmul(G, W)),
+             ("grad_W", lambda: torch.matmul(G.t(), H))]
+    stream = torch.cuda.current_stream()
+    res = []
+    for name, fn in cases:
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(1, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        res.append({"gemm": name, "ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                    "frac": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        print(f"{name}: {ms:.3f} ms {res[-1]['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    out = {"metric": "vendor BLAS (torch.matmul -> hipBLASLt) on the loss's contraction shapes, median launch",
+           "unit": "TFLOP/s", "n_gpus": 1, "peak": PEAK_BF16_TFLOPS, "dtype": "bf16",
+           "config": {"workload": f"{args.workload}: one chunk of {C} rows, d={d}, V={V}", "chunk": C},
+           "gemms": res}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     from chunked_top_kl_head_amd import synth
 
@@ -314,6 +363,9 @@ def main() -> int:
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="measure the part's sustained bf16 MFMA rate and clock with no memory traffic "
                          "(constant, changing and LDS-fed random operands)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor BLAS (torch.matmul) on the three contraction shapes of one chunk, "
+                         "plain bf16 outputs: a yardstick for the engine's per-launch rates")
     ap.add_argument("--copy-calibration-bytes", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many bytes (a kernel of known "
                          "traffic, used to scale the FETCH_SIZE/WRITE_SIZE counters of a profiling run)")
@@ -339,6 +391,8 @@ def main() -> int:
         return bench_teacher(args)
     if args.mfma_ceiling:
         return bench_mfma_ceiling(args)
+    if args.vendor_gemm:
+        return bench_vendor_gemm(args)
     wl = synth.WORKLOADS[args.workload]
     chunk = args.chunk or wl.chunk
     t_gen = time.perf_counter()
