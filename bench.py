@@ -373,7 +373,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the loss on a single GPU; positions shard naturally across GPUs "
+        print("bench.py: the library runs the loss on a single GPU; positions shard naturally across GPUs "
               "but no multi-GPU path is built. Run with --gpus 1.", file=sys.stderr, flush=True)
         return 2
 
