@@ -170,7 +170,7 @@ def test_schedules_agree_bitwise_on_logits():
     say("  lse and row losses bitwise equal across schedules; two-stage repeat bitwise equal")
 
 
-def _random_cases(n=10, seed=2026):
+def _random_cases(n=24, seed=2026):
     """Seeded random shapes: hidden sizes 8..520 (K tails inside a step, partial
     hidden tiles), vocabularies that are not multiples of 4, chunks from one row
     to all rows, temperatures 0.5..3, random masks; bf16 and fp32."""
@@ -189,7 +189,7 @@ def _random_cases(n=10, seed=2026):
     return cases
 
 
-def _random_medium_cases(n=4, seed=2027):
+def _random_medium_cases(n=6, seed=2027):
     """Seeded random problems whose chunks (2,049 rows up to all of T) put grad_W,
     and above 4,096 rows the logits and grad_H contractions too, on the engine's
     two-stage schedule, with random hidden and vocabulary tails."""
